@@ -1,0 +1,69 @@
+"""Layer-invariant attention control for one decode step.
+
+"GPT-OSS-120B giga-kernel decode", section "Kernel contract": per step the
+kernel consumes, built once from the per-layer metadata, a full block table and
+a trimmed sliding-window block table, an active mask, absolute and
+window-frame positions, and two KV-update indices (one for the full table, one
+for the trimmed sliding-window table).  Even layers use a window of 128 keys.
+
+Readings (design notes):
+  * ``seq_lens[b]`` counts the sequence's tokens including the new one; the
+    new token's index is ``p = seq_lens[b] - 1`` and the cache is indexed by
+    that token index, never by the absolute position.
+  * the window holds the ``W`` most recent tokens including the new one:
+    token indices ``[p - W + 1, p]``.  This is the only width for which the
+    early-eviction boundary described in "DI wiring (NIXL)" falls at
+    ``N % block_size == block_size - 1``.
+  * the trimmed table lists the sliding-window table's block ids for logical
+    blocks ``f .. p // Bk`` where ``f = max(0, p - W + 1) // Bk``, padded with
+    -1 to width ``ceil((W - 1) / Bk) + 1``; the window-frame position is
+    ``p - f * Bk``.
+  * an update index is the cache slot ``block_id * Bk + offset`` (int64);
+    inactive sequences get -1 everywhere (no write, no read, zero output), and
+    so does an update index whose table entry is negative (no block).
+"""
+import numpy as np
+
+
+def trimmed_width(window: int, block: int) -> int:
+    """Most logical blocks a ``window``-token span can touch."""
+    return -(-(window - 1) // block) + 1
+
+
+def attention_control(seq_lens, active, bt_full, bt_swa, block: int, window: int,
+                      positions=None):
+    """Return the per-step control as a dict of numpy arrays.
+
+    bt_full, bt_swa : int32 [B, width] tables indexed by logical block.
+    Keys: ``pos_full`` (int32 [B], p), ``pos_swa`` (int32 [B], window-frame
+    position), ``bt_swa_trim`` (int32 [B, n_swa]), ``upd_full`` and
+    ``upd_swa`` (int64 [B] cache slots), ``pos_abs`` (int64 [B], the absolute
+    positions carried for the rotary stage; -1 when not given or inactive).
+    """
+    seq_lens = np.asarray(seq_lens)
+    B = seq_lens.shape[0]
+    n_swa = trimmed_width(window, block)
+    pos_full = np.full(B, -1, dtype=np.int32)
+    pos_swa = np.full(B, -1, dtype=np.int32)
+    trim = np.full((B, n_swa), -1, dtype=np.int32)
+    upd_full = np.full(B, -1, dtype=np.int64)
+    upd_swa = np.full(B, -1, dtype=np.int64)
+    pos_abs = np.full(B, -1, dtype=np.int64)
+    for b in range(B):
+        if not active[b]:
+            continue
+        p = int(seq_lens[b]) - 1
+        pos_full[b] = p
+        blk_full = int(bt_full[b, p // block])
+        upd_full[b] = blk_full * block + p % block if blk_full >= 0 else -1
+        first = max(0, p - window + 1) // block
+        for c in range(first, p // block + 1):
+            trim[b, c - first] = bt_swa[b, c]
+        wf = p - first * block
+        pos_swa[b] = wf
+        blk_swa = int(trim[b, wf // block])
+        upd_swa[b] = blk_swa * block + wf % block if blk_swa >= 0 else -1
+        if positions is not None:
+            pos_abs[b] = int(positions[b])
+    return dict(pos_full=pos_full, pos_swa=pos_swa, bt_swa_trim=trim,
+                upd_full=upd_full, upd_swa=upd_swa, pos_abs=pos_abs)
