@@ -1,0 +1,94 @@
+// Attention-control setup and the quantising KV write, gfx950.
+//
+// Setup builds, once per step, the layer-invariant control the page
+// "GPT-OSS-120B giga-kernel decode" lists under "Kernel contract": the
+// trimmed sliding-window table, the absolute and window-frame positions and
+// the two KV-update indices.  The KV write quantises the new token's K/V to
+// OCP E4M3 and scatters them through an update index, K through the packed
+// view and V plain ("KV-cache layout").
+#include "pkv_device.hpp"
+#include "pkv_internal.hpp"
+
+namespace pkv {
+
+namespace {
+
+__global__ void __launch_bounds__(256) setup_kernel(SetupLaunch a) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b >= a.B) return;
+  const int BK = a.block;
+  const int len = a.seq_lens[b];
+  const bool act = a.active[b] != 0 && len > 0;
+  int32_t* trow = a.trim ? a.trim + static_cast<int64_t>(b) * a.trim_width : nullptr;
+  if (!act) {
+    a.pos_full[b] = -1;
+    a.upd_full[b] = -1;
+    if (a.window > 0) {
+      a.pos_swa[b] = -1;
+      a.upd_swa[b] = -1;
+      for (int i = 0; i < a.trim_width; ++i) trow[i] = -1;
+    }
+    if (a.pos_abs) a.pos_abs[b] = -1;
+    return;
+  }
+  const int p = len - 1;
+  const int cp = p / BK;
+  const bool in_table = cp < a.bt_width;
+  a.pos_full[b] = p;
+  {
+    const int blk = in_table ? a.bt_full[static_cast<int64_t>(b) * a.bt_full_stride + cp] : -1;
+    a.upd_full[b] = blk >= 0 ? static_cast<int64_t>(blk) * BK + p % BK : -1;
+  }
+  if (a.window > 0) {
+    const int first = max(0, p - a.window + 1) / BK;
+    const int32_t* srow = a.bt_swa + static_cast<int64_t>(b) * a.bt_swa_stride;
+    for (int i = 0; i < a.trim_width; ++i) {
+      const int c = first + i;
+      trow[i] = (c <= cp && c < a.bt_width) ? srow[c] : -1;
+    }
+    a.pos_swa[b] = p - first * BK;
+    const int blk = in_table ? srow[cp] : -1;
+    a.upd_swa[b] = blk >= 0 ? static_cast<int64_t>(blk) * BK + p % BK : -1;
+  }
+  if (a.pos_abs) a.pos_abs[b] = a.positions ? a.positions[b] : -1;
+}
+
+// one thread per (sequence, KV head, dimension)
+__global__ void __launch_bounds__(256) kv_update_kernel(UpdateLaunch a) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t n = static_cast<int64_t>(a.B) * a.Hkv * kHeadDim;
+  if (idx >= n) return;
+  const int j = static_cast<int>(idx % kHeadDim);
+  const int64_t bh = idx / kHeadDim;
+  const int h = static_cast<int>(bh % a.Hkv);
+  const int b = static_cast<int>(bh / a.Hkv);
+  const int64_t slot = a.slot[b];
+  const int BK = a.block;
+  if (slot < 0 || slot >= a.nb * BK) return;
+  const int64_t blk = slot / BK;
+  const int t = static_cast<int>(slot % BK);
+  const float kx = __fdiv_rn(bf16_bits_to_f32(a.k_new[idx]), a.k_scale);
+  const float vx = __fdiv_rn(bf16_bits_to_f32(a.v_new[idx]), a.v_scale);
+  const int64_t tile = (blk * a.Hkv + h) * static_cast<int64_t>(BK) * kHeadDim;
+  const int64_t koff = a.k_packed ? tile + (static_cast<int64_t>(t / 2) * kHeadDim + j) * 2 + (t & 1)
+                                  : tile + static_cast<int64_t>(t) * kHeadDim + j;
+  a.k[koff] = f32_to_e4m3_rne_sat(kx);
+  a.v[tile + static_cast<int64_t>(t) * kHeadDim + j] = f32_to_e4m3_rne_sat(vx);
+}
+
+}  // namespace
+
+hipError_t launch_setup(const SetupLaunch& L, hipStream_t stream) {
+  const int n_wg = (L.B + 255) / 256;
+  hipLaunchKernelGGL(setup_kernel, dim3(n_wg), dim3(256), 0, stream, L);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_update(const UpdateLaunch& L, hipStream_t stream) {
+  const int64_t n = static_cast<int64_t>(L.B) * L.Hkv * kHeadDim;
+  const int64_t n_wg = (n + 255) / 256;
+  hipLaunchKernelGGL(kv_update_kernel, dim3(static_cast<unsigned>(n_wg)), dim3(256), 0, stream, L);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -1,0 +1,562 @@
+// Paged decode attention over the packed-FP8 cache, gfx950.
+//
+// What it computes is decode attention read through the paged layout of the
+// page "GPT-OSS-120B giga-kernel decode": keys of sequence b are frame
+// positions [lo, hi] (hi = frame_pos[b]; lo = 0 for full layers and
+// hi - window + 1 for sliding-window layers, section "Kernel contract"), key t
+// sits in block table[b, t / BK] at slot t % BK, K stored through the packed
+// view [.., BK/2, 64, 2] and V plain [.., BK, 64] (section "KV-cache layout").
+//
+// Work decomposition (MI355X design, not from the pages):
+//  * The unit of work is a 32-token sub-tile of one (sequence, KV head) item.
+//    All items' sub-tiles are laid end to end; each wave takes one contiguous,
+//    equal share of that line (stream-K style), so ragged batches balance
+//    without any host-side knowledge of the lengths.
+//  * A wave works through its share item by item with its own online-softmax
+//    state.  An item that lies wholly in one wave is written out directly; an
+//    item cut by share boundaries leaves an fp32 partial (m, l, o) per piece,
+//    and the last piece to arrive (device-scope counter) merges them.
+//  * QK^T runs on v_mfma_f32_16x16x32_bf16 as S^T = Kp * Qx: the A operand is
+//    16 packed K rows of 64 token-pair bytes each (two tokens interleaved per
+//    dimension), B is the group's 8 queries expanded by token parity (column
+//    (g, e) holds q_g in the lanes of parity e and zeros in the other), so one
+//    16x16 tile yields the scores of 8 queries x 32 tokens with no byte
+//    shuffling of K.  The E4M3 -> bf16 conversion is exact.
+//  * PV runs on v_mfma_f32_16x16x32_f16 as O'^T = V'^T * P'^T: the scores
+//    stay in the lanes that produced them (column (g, e), tokens 8q+2r+e), and
+//    the V operand (8 consecutive tokens x one dimension per lane) is built
+//    from per-token dwords with v_perm_b32 + the packed fp8 -> fp16 convert.
+//    The two parity columns of a query are summed once at the end.
+//  * Online softmax in the log2 domain (k_scale, 1/sqrt(d) and log2(e) folded
+//    into one multiplier); the running maximum is only raised when some lane
+//    beats it by more than 2^8, so rescaling is rare and the PV weights stay
+//    below 256 (exact bookkeeping: numerator and denominator share the
+//    reference maximum).
+#include "pkv_device.hpp"
+#include "pkv_internal.hpp"
+
+namespace pkv {
+
+namespace {
+
+constexpr int kSub = 32;              // tokens per MFMA sub-tile
+constexpr int kWavesPerWG = 4;
+constexpr float kRescaleSlack = 8.0f; // log2 units
+// Waves per SIMD the kernel is compiled for (= workgroups per CU, 4 waves
+// each); the stream-K shares assume every worker is resident at once.
+constexpr int kWGPerCU = 3;
+
+struct AttnArgs {
+  const uint16_t* q;
+  const uint8_t* k;
+  const uint8_t* v;
+  const int32_t* table;
+  const int32_t* frame_pos;
+  uint16_t* out;
+  float* partial;
+  int32_t* counters;
+  int64_t nb;
+  int32_t B, Hq, Hkv, G;
+  int32_t bt_stride, table_width, window;
+  float score_scale;  // sm_scale * k_scale * log2(e)
+  float v_scale;
+  int32_t n_workers;
+};
+
+// frame range [lo, hi] of sequence b; returns the number of sub-tiles
+// (0 = no work: inactive, or invalid when *invalid is set).
+template <int BK, bool WINDOWED>
+__device__ __forceinline__ int seq_subtiles(const AttnArgs& a, int fp, int* lo_out,
+                                            bool* invalid) {
+  *invalid = false;
+  if (fp < 0) return 0;
+  if (fp >= a.table_width * BK) {
+    *invalid = true;
+    return 0;
+  }
+  const int lo = WINDOWED ? max(0, fp - a.window + 1) : 0;
+  *lo_out = lo;
+  return fp / kSub - lo / kSub + 1;
+}
+
+__device__ void block_exclusive_scan(int* s, int n) {
+  __shared__ int wsum[kWavesPerWG];
+  const int tid = threadIdx.x;
+  const int per = (n + 255) / 256;
+  const int beg = min(tid * per, n);
+  const int end = min(beg + per, n);
+  int local = 0;
+  for (int i = beg; i < end; ++i) local += s[i];
+  const int lane = tid & 63;
+  int x = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wsum[tid >> 6] = x;
+  __syncthreads();
+  int wave_off = 0;
+  for (int w = 0; w < (tid >> 6); ++w) wave_off += wsum[w];
+  int run = wave_off + x - local;
+  for (int i = beg; i < end; ++i) {
+    const int v = s[i];
+    s[i] = run;
+    run += v;
+  }
+  if (tid == 255) s[n] = wave_off + x;
+  __syncthreads();
+}
+
+__device__ __forceinline__ float wave_max_same_g(float v) {
+  v = fmaxf(v, __shfl_xor(v, 8, 64));
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  v = fmaxf(v, __shfl_xor(v, 32, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum_same_g(float v) {
+  v += __shfl_xor(v, 8, 64);
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+// Running state of one wave for one item (per lane: query g = m%8, parity e = m/8).
+struct State {
+  f32x4_t acc[4];  // acc[tau][r] = O'[(g,e)][dim 16q + 4r + tau] (unnormalised)
+  float m;         // reference maximum (log2 domain), identical in all lanes of g
+  float l;         // this lane's share of the denominator
+  bool bad;        // a table entry outside [0, nb) was met
+};
+
+struct Stage {
+  u32x4_t k0, k1;   // 32 bytes of packed K row (pair m), bytes [32q, 32q+32)
+  uint32_t v[8];    // V dwords: tokens 8q..8q+7, dims 4m..4m+3
+};
+
+template <int BK, bool WINDOWED>
+struct Item {
+  const uint8_t* kbase;
+  const uint8_t* vbase;
+  const int32_t* trow;
+  int64_t nb;
+  int hkv, h;
+  int clo, chi;         // first / last logical block holding keys
+  int tab_base;         // logical block held by lane 0 of `tab`
+  int tab;              // table entries for logical blocks tab_base + lane
+  bool bad;
+
+  __device__ Item(const AttnArgs& a, int b, int h_, int lo, int hi)
+      : kbase(a.k), vbase(a.v), nb(a.nb), hkv(a.Hkv), h(h_), bad(false) {
+    clo = lo / BK;
+    chi = hi / BK;
+    trow = a.table + static_cast<int64_t>(b) * a.bt_stride;
+    tab_base = -1000000;
+    tab = 0;
+  }
+
+  // Block id of logical block c (uniform c); refreshes the table window when
+  // c leaves it.  Out-of-range ids are replaced by 0 and flagged.
+  __device__ __forceinline__ int block_of(int c) {
+    if (c < tab_base || c >= tab_base + 64) {
+      tab_base = c;
+      const int cc = c + lane_id();
+      tab = (cc <= chi) ? trow[cc] : 0;
+    }
+    int blk = __builtin_amdgcn_readlane(tab, c - tab_base);
+    if (blk < 0 || static_cast<int64_t>(blk) >= nb) {
+      bad = true;
+      blk = 0;
+    }
+    return blk;
+  }
+
+  __device__ __forceinline__ int clampc(int c) const { return min(max(c, clo), chi); }
+
+  __device__ __forceinline__ void issue(Stage& st, int t32) {
+    const int lane = lane_id();
+    const int m = lane & 15, q = lane >> 4;
+    const int base = t32 * kSub;
+    // ---- K: pair row m of the sub-tile = tokens base+2m, base+2m+1
+    const uint8_t* kp;
+    const uint8_t* vp;
+    if constexpr (BK >= kSub) {
+      const int c = clampc(base / BK);
+      const int blk = block_of(c);
+      const int64_t tile = (static_cast<int64_t>(blk) * hkv + h) * (BK * kHeadDim);
+      const int tb = base % BK;
+      kp = kbase + tile + (tb / 2 + m) * (2 * kHeadDim) + 32 * q;
+      vp = vbase + tile + (tb + 8 * q) * kHeadDim + 4 * m;
+    } else {
+      // BK == 16: the sub-tile spans two blocks
+      const int c0 = clampc(base / BK), c1 = clampc(base / BK + 1);
+      const int blk0 = block_of(c0), blk1 = block_of(c1);
+      const int blk_k = (m < 8) ? blk0 : blk1;
+      const int blk_v = (q < 2) ? blk0 : blk1;
+      const int64_t tk = (static_cast<int64_t>(blk_k) * hkv + h) * (BK * kHeadDim);
+      const int64_t tv = (static_cast<int64_t>(blk_v) * hkv + h) * (BK * kHeadDim);
+      kp = kbase + tk + (m & 7) * (2 * kHeadDim) + 32 * q;
+      vp = vbase + tv + ((8 * q) & 15) * kHeadDim + 4 * m;
+    }
+    st.k0 = *reinterpret_cast<const u32x4_t*>(kp);
+    st.k1 = *reinterpret_cast<const u32x4_t*>(kp + 16);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st.v[i] = *reinterpret_cast<const uint32_t*>(vp + i * kHeadDim);
+  }
+};
+
+template <int BK, bool WINDOWED>
+__device__ __forceinline__ void compute_subtile(const AttnArgs& a, Stage& st, int t32, int lo,
+                                                int hi, const uint32_t (&qx)[4][4], State& s) {
+  const int lane = lane_id();
+  const int m = lane & 15, q = lane >> 4, e = m >> 3;
+  const int base = t32 * kSub;
+  const bool interior = (base >= lo) && (base + kSub - 1 <= hi);
+  uint32_t kd[8] = {st.k0[0], st.k0[1], st.k0[2], st.k0[3], st.k1[0], st.k1[1], st.k1[2], st.k1[3]};
+  if (!interior) {
+    // zero the bytes of out-of-range tokens so 0 * NaN never reaches a score
+    const int t_even = base + 2 * m;
+    const bool ok0 = (t_even >= lo) && (t_even <= hi);
+    const bool ok1 = (t_even + 1 >= lo) && (t_even + 1 <= hi);
+    const uint32_t keep = (ok0 ? 0x00ff00ffu : 0u) | (ok1 ? 0xff00ff00u : 0u);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) kd[i] &= keep;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int t = base + 8 * q + i;
+      if (t < lo || t > hi) st.v[i] = 0u;
+    }
+  }
+  // ---- S^T = Kp * Qx
+  f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t av[4] = {e4m3x2_to_bf16x2<false>(kd[2 * i]), e4m3x2_to_bf16x2<true>(kd[2 * i]),
+                      e4m3x2_to_bf16x2<false>(kd[2 * i + 1]), e4m3x2_to_bf16x2<true>(kd[2 * i + 1])};
+    bf16x8_t A = __builtin_bit_cast(bf16x8_t, av);
+    bf16x8_t Bq = __builtin_bit_cast(bf16x8_t, qx[i]);
+    sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bq, sacc, 0, 0, 0);
+  }
+  // lane holds scores of query g for tokens base + 8q + 2r + e
+  float x[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    x[r] = sacc[r] * a.score_scale;
+    if (!interior) {
+      const int t = base + 8 * q + 2 * r + e;
+      if (t < lo || t > hi) x[r] = -INFINITY;
+    }
+  }
+  const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+  if (__any(mx > s.m + kRescaleSlack)) {
+    const float mnew = fmaxf(s.m, wave_max_same_g(mx));
+    const float alpha = __builtin_amdgcn_exp2f(s.m - mnew);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) s.acc[t] *= alpha;
+    s.l *= alpha;
+    s.m = mnew;
+  }
+  uint32_t pv[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float p = __builtin_amdgcn_exp2f(x[r] - s.m);
+    s.l += p;
+    const _Float16 ph = static_cast<_Float16>(p);
+    pv[r] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, ph)) << (16 * e);
+  }
+  f16x8_t Bp = __builtin_bit_cast(f16x8_t, pv);
+  // ---- V operands: dims 4m+tau, tokens 8q .. 8q+7 in slot order
+  uint32_t vop[4][4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t lo2 = __builtin_amdgcn_perm(st.v[2 * k + 1], st.v[2 * k], 0x05010400u);
+    const uint32_t hi2 = __builtin_amdgcn_perm(st.v[2 * k + 1], st.v[2 * k], 0x07030602u);
+    vop[0][k] = e4m3x2_to_f16x2<false>(lo2);
+    vop[1][k] = e4m3x2_to_f16x2<true>(lo2);
+    vop[2][k] = e4m3x2_to_f16x2<false>(hi2);
+    vop[3][k] = e4m3x2_to_f16x2<true>(hi2);
+  }
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    f16x8_t Av = __builtin_bit_cast(f16x8_t, vop[t]);
+    s.acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Av, Bp, s.acc[t], 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void store_bf16x16(uint16_t* dst, const float* v) {
+  uint32_t w[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    w[i] = static_cast<uint32_t>(f32_to_bf16_bits(v[2 * i])) |
+           (static_cast<uint32_t>(f32_to_bf16_bits(v[2 * i + 1])) << 16);
+  u32x4_t* d = reinterpret_cast<u32x4_t*>(dst);
+  d[0] = u32x4_t{w[0], w[1], w[2], w[3]};
+  d[1] = u32x4_t{w[4], w[5], w[6], w[7]};
+}
+
+constexpr int kSlotFloats = 8 * kHeadDim + 16;  // o[8][64], m[8], l[8]
+
+template <int BK, bool WINDOWED>
+__global__ void __launch_bounds__(256, kWGPerCU) decode_attn_kernel(AttnArgs a) {
+  extern __shared__ int s_pre[];  // [B + 1] prefix of per-sequence sub-tile counts
+  const int tid = threadIdx.x;
+  const int B = a.B;
+  for (int b = tid; b < B; b += 256) {
+    int lo = 0;
+    bool inv;
+    s_pre[b] = seq_subtiles<BK, WINDOWED>(a, a.frame_pos[b], &lo, &inv);
+  }
+  __syncthreads();
+  block_exclusive_scan(s_pre, B);
+
+  // rows with no work: +0 for inactive sequences, NaN for invalid positions
+  for (int b = blockIdx.x; b < B; b += gridDim.x) {
+    if (s_pre[b + 1] != s_pre[b]) continue;
+    int lo = 0;
+    bool inv;
+    seq_subtiles<BK, WINDOWED>(a, a.frame_pos[b], &lo, &inv);
+    const uint16_t fill = inv ? 0x7fc0u : 0u;
+    const uint32_t f2 = static_cast<uint32_t>(fill) * 0x10001u;
+    u32x4_t* row = reinterpret_cast<u32x4_t*>(a.out + static_cast<int64_t>(b) * a.Hq * kHeadDim);
+    for (int i = tid; i < a.Hq * kHeadDim / 8; i += 256) row[i] = u32x4_t{f2, f2, f2, f2};
+  }
+
+  const int lane = tid & 63;
+  const int m = lane & 15, q = lane >> 4, e = m >> 3, g = m & 7;
+  const int wid = blockIdx.x * kWavesPerWG + (tid >> 6);
+  const int64_t total = static_cast<int64_t>(s_pre[B]) * a.Hkv;
+  if (total == 0) return;
+  const int64_t chunk = (total + a.n_workers - 1) / a.n_workers;
+  int64_t cur = static_cast<int64_t>(wid) * chunk;
+  const int64_t wend = min(cur + chunk, total);
+  if (cur >= wend) return;
+  const int64_t wbeg = cur;
+
+  // locate the first item: the last b with s_pre[b] * Hkv <= cur
+  int b;
+  {
+    int lo_i = 0, hi_i = B - 1;
+    while (lo_i < hi_i) {
+      const int mid = (lo_i + hi_i + 1) >> 1;
+      if (static_cast<int64_t>(s_pre[mid]) * a.Hkv <= cur) lo_i = mid; else hi_i = mid - 1;
+    }
+    b = lo_i;
+  }
+  int n = s_pre[b + 1] - s_pre[b];
+  int64_t rel = cur - static_cast<int64_t>(s_pre[b]) * a.Hkv;
+  int h = static_cast<int>(rel / n);
+  int j = static_cast<int>(rel % n);
+
+  while (cur < wend && b < B) {
+    n = s_pre[b + 1] - s_pre[b];
+    const int seg = static_cast<int>(min(static_cast<int64_t>(n - j), wend - cur));
+    const int64_t item_beg = static_cast<int64_t>(s_pre[b]) * a.Hkv + static_cast<int64_t>(h) * n;
+    const int64_t item_end = item_beg + n;
+    const int hi = a.frame_pos[b];
+    const int lo = WINDOWED ? max(0, hi - a.window + 1) : 0;
+
+    // expanded queries: qx[i][k] holds q[g][16q + 4i + k] in the half of parity e
+    uint32_t qx[4][4];
+    {
+      u32x4_t q0 = {0u, 0u, 0u, 0u}, q1 = {0u, 0u, 0u, 0u};
+      if (g < a.G) {
+        const uint16_t* qp =
+            a.q + (static_cast<int64_t>(b) * a.Hq + h * a.G + g) * kHeadDim + 16 * q;
+        q0 = *reinterpret_cast<const u32x4_t*>(qp);
+        q1 = *reinterpret_cast<const u32x4_t*>(qp + 8);
+      }
+      const uint32_t qw[8] = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int d = 4 * i + k;  // dim 16q + d
+          const uint32_t bits = (qw[d >> 1] >> (16 * (d & 1))) & 0xffffu;
+          qx[i][k] = bits << (16 * e);
+        }
+    }
+
+    Item<BK, WINDOWED> it(a, b, h, lo, hi);
+    State s;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) s.acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    s.m = -INFINITY;
+    s.l = 0.f;
+    const int t0 = lo / kSub + j;
+    const int tlast = t0 + seg - 1;
+
+    // two-stage software pipeline over the segment's sub-tiles
+    Stage sa, sb;
+    it.issue(sa, t0);
+    for (int i = 0; i < seg; i += 2) {
+      it.issue(sb, min(t0 + i + 1, tlast));
+      compute_subtile<BK, WINDOWED>(a, sa, t0 + i, lo, hi, qx, s);
+      if (i + 1 >= seg) break;
+      it.issue(sa, min(t0 + i + 2, tlast));
+      compute_subtile<BK, WINDOWED>(a, sb, t0 + i + 1, lo, hi, qx, s);
+    }
+    s.bad = it.bad;
+
+    // ---- finish the piece
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s.acc[t][r] += __shfl_xor(s.acc[t][r], 8, 64);
+    const float lsum = wave_sum_same_g(s.l);
+    const bool bad = __any(s.bad);
+    // dims in lane order: o[4r + tau] = dim 16q + 4r + tau
+    float o[16];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) o[4 * r + t] = s.acc[t][r];
+
+    const bool whole = (item_beg >= wbeg) && (item_end <= wend);
+    if (whole) {
+      if (e == 0 && g < a.G) {
+        const float f = bad ? NAN : a.v_scale / lsum;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[i] *= f;
+        store_bf16x16(a.out + (static_cast<int64_t>(b) * a.Hq + h * a.G + g) * kHeadDim + 16 * q, o);
+      }
+    } else {
+      const int64_t wfirst = item_beg / chunk, wlast = (item_end - 1) / chunk;
+      const int slot = (item_beg >= wbeg) ? 2 * wid + 1 : 2 * wid;
+      float* ps = a.partial + static_cast<int64_t>(slot) * kSlotFloats;
+      if (e == 0) {
+        f32x4_t* po = reinterpret_cast<f32x4_t*>(ps + g * kHeadDim + 16 * q);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) po[i] = f32x4_t{o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
+        if (q == 0) {
+          ps[8 * kHeadDim + g] = s.m;
+          ps[8 * kHeadDim + 8 + g] = bad ? NAN : lsum;
+        }
+      }
+      __threadfence();
+      int old = 0;
+      int32_t* ctr = a.counters + static_cast<int64_t>(b) * a.Hkv + h;
+      if (lane == 0) old = atomicAdd(ctr, 1);
+      old = __shfl(old, 0, 64);
+      const int ncontrib = static_cast<int>(wlast - wfirst + 1);
+      if (old == ncontrib - 1) {
+        __threadfence();
+        // merge every piece of the item: first worker's tail slot, then the
+        // head slots of the following workers
+        float mm = -INFINITY;
+        for (int k = 0; k < ncontrib; ++k) {
+          const int sl = (k == 0) ? static_cast<int>(2 * wfirst + 1) : static_cast<int>(2 * (wfirst + k));
+          mm = fmaxf(mm, __builtin_nontemporal_load(a.partial + static_cast<int64_t>(sl) * kSlotFloats + 8 * kHeadDim + g));
+        }
+        float acc[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+        float ltot = 0.f;
+        for (int k = 0; k < ncontrib; ++k) {
+          const int sl = (k == 0) ? static_cast<int>(2 * wfirst + 1) : static_cast<int>(2 * (wfirst + k));
+          const float* pk = a.partial + static_cast<int64_t>(sl) * kSlotFloats;
+          const float mk = __builtin_nontemporal_load(pk + 8 * kHeadDim + g);
+          const float lk = __builtin_nontemporal_load(pk + 8 * kHeadDim + 8 + g);
+          const float w = __builtin_amdgcn_exp2f(mk - mm);
+          ltot += w * lk;
+          if (e == 0) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              acc[i] += w * __builtin_nontemporal_load(pk + g * kHeadDim + 16 * q + i);
+          }
+        }
+        if (e == 0 && g < a.G) {
+          const float f = a.v_scale / ltot;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[i] *= f;
+          store_bf16x16(a.out + (static_cast<int64_t>(b) * a.Hq + h * a.G + g) * kHeadDim + 16 * q, acc);
+        }
+        if (lane == 0) *ctr = 0;
+      }
+    }
+
+    cur += seg;
+    j = 0;
+    if (++h == a.Hkv) {
+      h = 0;
+      do {
+        ++b;
+      } while (b < B && s_pre[b + 1] == s_pre[b]);
+    }
+  }
+}
+
+template <int BK, bool WINDOWED>
+hipError_t launch(const AttnArgs& a, int n_wg, size_t lds, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_attn_kernel<BK, WINDOWED>), dim3(n_wg), dim3(256), lds, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int attn_workers(int64_t batch, int kv_heads, int max_subtiles) {
+  const int64_t total = batch * kv_heads * static_cast<int64_t>(max_subtiles);
+  int64_t w = (total + kMinSubtilesPerWorker - 1) / kMinSubtilesPerWorker;
+  w = (w + kWavesPerWG - 1) / kWavesPerWG * kWavesPerWG;
+  if (w < kWavesPerWG) w = kWavesPerWG;
+  if (w > kMaxWorkers) w = kMaxWorkers;
+  return static_cast<int>(w);
+}
+
+int attn_max_subtiles(int block, int table_width, int window) {
+  int64_t keys = static_cast<int64_t>(table_width) * block;
+  if (window > 0 && window < keys) keys = window;
+  return static_cast<int>((keys + kSub - 1) / kSub + 1);
+}
+
+int64_t attn_workspace_bytes(int64_t batch, int kv_heads, int n_workers) {
+  const int64_t ctr = (batch * kv_heads * 4 + 255) / 256 * 256;
+  return ctr + static_cast<int64_t>(2) * n_workers * kSlotFloats * 4;
+}
+
+hipError_t launch_decode_attn(const AttnLaunch& L, hipStream_t stream) {
+  AttnArgs a;
+  a.q = L.q;
+  a.k = L.k;
+  a.v = L.v;
+  a.table = L.table;
+  a.frame_pos = L.frame_pos;
+  a.out = L.out;
+  const int64_t ctr = (static_cast<int64_t>(L.B) * L.Hkv * 4 + 255) / 256 * 256;
+  a.counters = reinterpret_cast<int32_t*>(L.workspace);
+  a.partial = reinterpret_cast<float*>(reinterpret_cast<char*>(L.workspace) + ctr);
+  a.nb = L.nb;
+  a.B = L.B;
+  a.Hq = L.Hq;
+  a.Hkv = L.Hkv;
+  a.G = L.Hq / L.Hkv;
+  a.bt_stride = L.bt_stride;
+  a.table_width = L.table_width;
+  a.window = L.window;
+  a.score_scale = L.sm_scale * L.k_scale * 1.4426950408889634f;
+  a.v_scale = L.v_scale;
+  a.n_workers = L.n_workers;
+  // the workspace holds partial slots for at most this many workers
+  if (a.n_workers < kWavesPerWG || a.n_workers > kMaxWorkers || a.n_workers % kWavesPerWG)
+    return hipErrorInvalidValue;
+  // never launch more workers than can be resident together
+  static int cu_count[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
+    if (!cu_count[dev])
+      (void)hipDeviceGetAttribute(&cu_count[dev], hipDeviceAttributeMultiprocessorCount, dev);
+    const int resident = cu_count[dev] * kWGPerCU * kWavesPerWG;
+    if (resident >= kWavesPerWG && a.n_workers > resident) a.n_workers = resident;
+  }
+  const int n_wg = a.n_workers / kWavesPerWG;
+  const size_t lds = static_cast<size_t>(L.B + 1) * sizeof(int);
+  const bool win = L.window > 0;
+  switch (L.block) {
+    case 16: return win ? launch<16, true>(a, n_wg, lds, stream) : launch<16, false>(a, n_wg, lds, stream);
+    case 32: return win ? launch<32, true>(a, n_wg, lds, stream) : launch<32, false>(a, n_wg, lds, stream);
+    case 64: return win ? launch<64, true>(a, n_wg, lds, stream) : launch<64, false>(a, n_wg, lds, stream);
+    case 128: return win ? launch<128, true>(a, n_wg, lds, stream) : launch<128, false>(a, n_wg, lds, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pkv

@@ -1,0 +1,66 @@
+// Internal launch interfaces between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kHeadDimSupported = 64;   // the only head size the kernels are built for
+constexpr int kMaxWorkers = 4096;          // waves of one attention launch (16 per CU on 256 CUs)
+constexpr int kMinSubtilesPerWorker = 8;   // 32-token sub-tiles; smaller shares only add partials
+constexpr int kMaxBatch = 8192;            // per-sequence prefix scan lives in LDS
+
+struct AttnLaunch {
+  const uint16_t* q;
+  const uint8_t* k;
+  const uint8_t* v;
+  const int32_t* table;
+  const int32_t* frame_pos;
+  uint16_t* out;
+  void* workspace;
+  int64_t nb;
+  int32_t B, Hq, Hkv, block;
+  int32_t bt_stride, table_width, window;
+  float k_scale, v_scale, sm_scale;
+  int32_t n_workers;
+};
+
+int attn_max_subtiles(int block, int table_width, int window);
+int attn_workers(int64_t batch, int kv_heads, int max_subtiles);
+int64_t attn_workspace_bytes(int64_t batch, int kv_heads, int n_workers);
+hipError_t launch_decode_attn(const AttnLaunch& L, hipStream_t stream);
+
+struct SetupLaunch {
+  int32_t B, block, window;
+  const int32_t* seq_lens;
+  const uint8_t* active;
+  const int64_t* positions;
+  const int32_t* bt_full;
+  int32_t bt_full_stride;
+  const int32_t* bt_swa;
+  int32_t bt_swa_stride, bt_width;
+  int32_t* pos_full;
+  int32_t* pos_swa;
+  int32_t* trim;
+  int32_t trim_width;
+  int64_t* upd_full;
+  int64_t* upd_swa;
+  int64_t* pos_abs;
+};
+hipError_t launch_setup(const SetupLaunch& L, hipStream_t stream);
+
+struct UpdateLaunch {
+  int32_t B, Hkv, block;
+  int64_t nb;
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint8_t* k;
+  uint8_t* v;
+  int32_t k_packed;
+  const int64_t* slot;
+  float k_scale, v_scale;
+};
+hipError_t launch_kv_update(const UpdateLaunch& L, hipStream_t stream);
+
+}  // namespace pkv
