@@ -1,0 +1,294 @@
+"""Benchmark: one decode step of paged attention over the packed-FP8 KV cache.
+
+A step is the whole path: the layer-invariant control setup, then for each of
+36 layers (alternating sliding-window 128 / full, 18 shared buffers) the
+quantising KV write and the paged decode attention, all through libpkv on one
+stream.  Workload: batch 64, 64 query / 8 KV heads, head_dim 64, block 32,
+every context 8192 tokens, random block tables, synthetic N(0,1) data.
+
+Prints one JSON line.  `value` is the step's algorithmic KV bytes (K + V FP8
+of every attended key of every layer) divided by the measured step time,
+in GB/s; tokens/s is batch / step time.  The step is replayed as a HIP graph
+(inputs resident in HBM); a second, eager phase brackets every full-layer
+attention launch with events on the launch stream to get the dominant
+kernel's average duration for the roofline.  `cpu_baseline` times the CPU
+oracle on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+    python bench.py --calibrate-copy      # plain device copy, for counter scaling
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = ["paged_fp8_kv_amd/csrc/decode_attn.hip", "paged_fp8_kv_amd/csrc/pkv_device.hpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_attn_full_cfg3_traffic.json")
+
+
+def kernel_sha():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kv_bytes_per_layer(wl, kind):
+    c = wl.cfg
+    n = wl.seq_lens.astype(np.int64)
+    if kind == "swa":
+        n = np.minimum(n, c.window)
+    n = np.where(wl.active > 0, n, 0)
+    return int(n.sum()) * c.hkv * 2 * c.head_dim
+
+
+def calibrate_copy(steps):
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n, "launches": steps}), flush=True)
+
+
+def cpu_baseline(wl, bufs_dev, seconds):
+    """Time the oracle's paged attention for one full layer over as many
+    sequences as fit in `seconds` (single thread)."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention as OA
+    c = wl.cfg
+    layer = 1 if c.kinds[1] == "full" else 0
+    host = bufs_dev[layer // 2].cpu().numpy()
+    half = wl.half_bytes
+    kh, vh = host[:half], host[half:]
+    q = wl.q[layer].float().numpy().astype(np.float64)
+    pos = (wl.seq_lens - 1).astype(np.int64)
+    done_bytes, rows = 0, 0
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        for b in range(c.batch):
+            OA.paged_decode_attention(q, kh, vh, wl.bt_full, pos, 0, c.block, c.hkv,
+                                      wl.k_scale[layer], wl.v_scale[layer],
+                                      1.0 / np.sqrt(c.head_dim), True, rows=[b])
+            done_bytes += int(wl.seq_lens[b]) * c.hkv * 2 * c.head_dim
+            rows += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        dt = time.perf_counter() - t0
+    return {"value": round(done_bytes / dt / 1e9, 6), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{rows} of {c.batch} sequences of one full-attention layer "
+                      f"({done_bytes / 1e6:.1f} MB of KV) in {dt:.1f} s, numpy float64, 1 thread"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="cfg3")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the decode step is data-parallel over sequences and KV heads, see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.calibrate_copy:
+        calibrate_copy(max(args.steps, 1))
+        return
+
+    import paged_fp8_kv_amd as P
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    cfg = W.CONFIGS[args.config]
+    hbm = torch.cuda.mem_get_info(dev)[1]
+    wl = W.make_workload(cfg, hbm_bytes=hbm)
+    log(f"workload {cfg.name}: nb={wl.nb}, {cfg.n_buffers} buffers of "
+        f"{2 * wl.half_bytes / 1e9:.2f} GB")
+    bufs = []
+    for j in range(cfg.n_buffers):
+        t = torch.empty(2 * wl.half_bytes, dtype=torch.uint8, device=dev)
+        W.fill_buffer(t, wl, j)
+        bufs.append(t)
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    seq_lens, active = to(wl.seq_lens.astype(np.int32)), to(wl.active)
+    positions = to(wl.positions.astype(np.int64))
+    bt_full, bt_swa = to(wl.bt_full), to(wl.bt_swa)
+    q, k_new, v_new = wl.q.to(dev), wl.k_new.to(dev), wl.v_new.to(dev)
+    has_swa = "swa" in cfg.kinds
+    win = cfg.window if has_swa else 0
+    ctl = P.pkv_setup_attn_control(seq_lens, active, bt_full, bt_swa, cfg.block, win,
+                                   positions=positions)
+    tw = ctl["bt_swa_trim"].shape[1]
+    ws_full = P.new_workspace(cfg.batch, cfg.hq, cfg.hkv, cfg.head_dim, cfg.block,
+                              wl.bt_full.shape[1], 0, dev)
+    ws_swa = P.new_workspace(cfg.batch, cfg.hq, cfg.hkv, cfg.head_dim, cfg.block, tw, win,
+                             dev) if has_swa else None
+    outs = [torch.empty_like(q[i]) for i in range(cfg.layers)]
+    sm = 1.0 / float(np.sqrt(cfg.head_dim))
+    alternating = all(k == ("swa" if i % 2 == 0 else "full") for i, k in enumerate(cfg.kinds))
+    step_desc = P.make_step(bufs, ctl, bt_full, cfg.batch, cfg.hq, cfg.hkv, cfg.head_dim,
+                            cfg.block, cfg.window, wl.nb) if alternating else None
+
+    def attn(i):
+        swa = cfg.kinds[i] == "swa"
+        buf = bufs[i // 2]
+        if swa:
+            P.pkv_paged_decode_attn(q[i], buf, ctl["bt_swa_trim"], ctl["pos_swa"], cfg.block,
+                                    wl.nb, cfg.window, wl.k_scale[i], wl.v_scale[i], sm, cfg.hkv,
+                                    out=outs[i], workspace=ws_swa)
+        else:
+            P.pkv_paged_decode_attn(q[i], buf, bt_full, ctl["pos_full"], cfg.block, wl.nb, 0,
+                                    wl.k_scale[i], wl.v_scale[i], sm, cfg.hkv, out=outs[i],
+                                    workspace=ws_full)
+
+    def update(i):
+        swa = cfg.kinds[i] == "swa"
+        P.pkv_kv_cache_update(bufs[i // 2], k_new[i], v_new[i],
+                              ctl["upd_swa"] if swa else ctl["upd_full"], cfg.block, wl.nb,
+                              wl.k_scale[i], wl.v_scale[i])
+
+    def step():
+        P.pkv_setup_attn_control(seq_lens, active, bt_full, bt_swa, cfg.block, win,
+                                 positions=positions, out=ctl)
+        for i in range(cfg.layers):
+            if step_desc is not None:
+                P.pkv_decode_layer(step_desc, i, q[i], k_new[i], v_new[i], wl.k_scale[i],
+                                   wl.v_scale[i], sm, outs[i], ws_swa if i % 2 == 0 else ws_full)
+            else:
+                update(i)
+                attn(i)
+
+    # eager warm-up; after the first step the cache holds this step's tokens,
+    # so every later step recomputes identical outputs
+    for _ in range(max(args.warmup, 1)):
+        step()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+
+    use_graph = not args.no_graph
+    g = None
+    if use_graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for r in range(3):
+            for o in outs:
+                o.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            if not all(torch.equal(a, b) for a, b in zip(outs, ref)):
+                log("graph replay differs from the eager step; timing eagerly")
+                use_graph = False
+                break
+        for _ in range(args.warmup):
+            g.replay() if use_graph else step()
+        torch.cuda.synchronize()
+
+    # ---- timed region: whole steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        g.replay() if use_graph else step()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms = dt * 1e3 / args.steps
+
+    # ---- dominant kernel: full-layer attention, bracketed by events on its stream
+    full_layers = [i for i, k in enumerate(cfg.kinds) if k == "full"]
+    swa_layers = [i for i, k in enumerate(cfg.kinds) if k == "swa"]
+    ev = []
+    ev_swa = []
+    n_ev_steps = max(1, min(args.steps, 5))
+    torch.cuda.synchronize()
+    for _ in range(n_ev_steps):
+        P.pkv_setup_attn_control(seq_lens, active, bt_full, bt_swa, cfg.block, win,
+                                 positions=positions, out=ctl)
+        for i in range(cfg.layers):
+            update(i)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            attn(i)
+            b.record()
+            (ev if cfg.kinds[i] == "full" else ev_swa).append((a, b))
+    torch.cuda.synchronize()
+    full_us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    swa_us = float(np.mean([a.elapsed_time(b) for a, b in ev_swa])) * 1e3 if ev_swa else None
+    for a, b in zip(outs, ref):
+        assert torch.equal(a, b), "outputs changed between steps"
+
+    step_bytes = sum(kv_bytes_per_layer(wl, k) for k in cfg.kinds)
+    full_bytes = kv_bytes_per_layer(wl, "full")
+    achieved = full_bytes / (full_us * 1e-6) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        tr = json.load(open(TRAFFIC_FILE))
+        if tr.get("kernel_sha") == kernel_sha() and tr.get("config") == args.config:
+            traffic = tr.get("bytes_per_launch")
+    value = step_bytes / (ms * 1e-3) / 1e9
+    result = {
+        "metric": "decode-attention KV GB/s (% of HBM peak) and tokens/s/GPU at batch 64",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3-kv/bf16-q/fp32-acc",
+        "data": "synthetic (seeded N(0,1) activations, FP8 history, random block tables)",
+        "config": {"workload": cfg.name, "layers": cfg.layers, "batch": cfg.batch,
+                   "q_heads": cfg.hq, "kv_heads": cfg.hkv, "head_dim": cfg.head_dim,
+                   "block": cfg.block, "context": "8192" if cfg.ctx[0] == "fixed" else str(cfg.ctx),
+                   "window": cfg.window, "num_blocks": wl.nb, "graph": use_graph},
+        "tokens_per_s": round(cfg.batch / (ms * 1e-3), 1),
+        "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
+        "kv_bytes_per_step": step_bytes,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "kernel": f"decode_attn_kernel<{cfg.block}, false> (full layers)",
+                     "bytes_per_launch": full_bytes, "avg_launch_us": round(full_us, 2),
+                     "swa_avg_launch_us": round(swa_us, 2) if swa_us else None},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, bufs, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -40,11 +40,24 @@ namespace pkv {
 namespace {
 
 constexpr int kSub = 32;              // tokens per MFMA sub-tile
-constexpr int kWavesPerWG = 4;
+#ifndef PKV_WAVES_PER_WG
+#define PKV_WAVES_PER_WG 4
+#endif
+constexpr int kWavesPerWG = PKV_WAVES_PER_WG;
+constexpr int kThreads = 64 * kWavesPerWG;
 constexpr float kRescaleSlack = 8.0f; // log2 units
+#ifndef PKV_DEPTH
+#define PKV_DEPTH 6
+#endif
+constexpr int kDepth = PKV_DEPTH;     // sub-tiles in flight per wave
+constexpr int kChunksPerWorker = 2;   // chunks of the item line per wave, on average
+constexpr int kMinChunk = 8;          // sub-tiles
 // Waves per SIMD the kernel is compiled for (= workgroups per CU, 4 waves
 // each); the stream-K shares assume every worker is resident at once.
-constexpr int kWGPerCU = 3;
+#ifndef PKV_WG_PER_CU
+#define PKV_WG_PER_CU 1
+#endif
+constexpr int kWGPerCU = PKV_WG_PER_CU;
 
 struct AttnArgs {
   const uint16_t* q;
@@ -54,7 +67,8 @@ struct AttnArgs {
   const int32_t* frame_pos;
   uint16_t* out;
   float* partial;
-  int32_t* counters;
+  int32_t* counters;  // [B * Hkv] arrival counters of split items
+  int32_t* queue;     // [2]: next chunk, waves that have left
   int64_t nb;
   int32_t B, Hq, Hkv, G;
   int32_t bt_stride, table_width, window;
@@ -82,7 +96,7 @@ __device__ __forceinline__ int seq_subtiles(const AttnArgs& a, int fp, int* lo_o
 __device__ void block_exclusive_scan(int* s, int n) {
   __shared__ int wsum[kWavesPerWG];
   const int tid = threadIdx.x;
-  const int per = (n + 255) / 256;
+  const int per = (n + kThreads - 1) / kThreads;
   const int beg = min(tid * per, n);
   const int end = min(beg + per, n);
   int local = 0;
@@ -104,8 +118,25 @@ __device__ void block_exclusive_scan(int* s, int n) {
     s[i] = run;
     run += v;
   }
-  if (tid == 255) s[n] = wave_off + x;
+  if (tid == kThreads - 1) s[n] = wave_off + x;
   __syncthreads();
+}
+
+// Cross-workgroup hand-off of split-KV partials.  Partials are written and
+// read with agent-scope relaxed atomics (write-through / coherent accesses),
+// and the writer waits for its stores to complete before it bumps the arrival
+// counter.  This avoids agent-scope release/acquire fences, which on this
+// target write back and invalidate the whole L2 of the issuing XCD.
+__device__ __forceinline__ void st_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_vm_stores() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): every issued store has completed
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 __device__ __forceinline__ float wave_max_same_g(float v) {
@@ -129,6 +160,14 @@ struct State {
   bool bad;        // a table entry outside [0, nb) was met
 };
 
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+// dword 3 of a raw (untyped, unswizzled) buffer resource on this target
+constexpr int kRsrcWord3 = 0x00020000;
+__device__ __forceinline__ rsrc_t tile_rsrc(const uint8_t* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p), static_cast<short>(0), bytes,
+                                           kRsrcWord3);
+}
+
 struct Stage {
   u32x4_t k0, k1;   // 32 bytes of packed K row (pair m), bytes [32q, 32q+32)
   uint32_t v[8];    // V dwords: tokens 8q..8q+7, dims 4m..4m+3
@@ -139,7 +178,7 @@ struct Item {
   const uint8_t* kbase;
   const uint8_t* vbase;
   const int32_t* trow;
-  int64_t nb;
+  int nb32;             // num_blocks clamped to int32 (block ids are int32)
   int hkv, h;
   int clo, chi;         // first / last logical block holding keys
   int tab_base;         // logical block held by lane 0 of `tab`
@@ -147,7 +186,8 @@ struct Item {
   bool bad;
 
   __device__ Item(const AttnArgs& a, int b, int h_, int lo, int hi)
-      : kbase(a.k), vbase(a.v), nb(a.nb), hkv(a.Hkv), h(h_), bad(false) {
+      : kbase(a.k), vbase(a.v), hkv(a.Hkv), h(h_), bad(false) {
+    nb32 = a.nb > 0x7fffffff ? 0x7fffffff : static_cast<int>(a.nb);
     clo = lo / BK;
     chi = hi / BK;
     trow = a.table + static_cast<int64_t>(b) * a.bt_stride;
@@ -155,16 +195,20 @@ struct Item {
     tab = 0;
   }
 
-  // Block id of logical block c (uniform c); refreshes the table window when
-  // c leaves it.  Out-of-range ids are replaced by 0 and flagged.
+  // Load the table entries of logical blocks c0 .. c0+63 (one per lane).
+  // Done between pipelined runs only, so no table load is ever pending while
+  // K/V loads are in flight.
+  __device__ __forceinline__ void load_window(int c0) {
+    tab_base = c0;
+    const int cc = c0 + lane_id();
+    tab = (cc <= chi) ? trow[cc] : 0;
+  }
+
+  // Block id of logical block c (uniform, inside the loaded window).
+  // Out-of-range ids are replaced by 0 and flagged.
   __device__ __forceinline__ int block_of(int c) {
-    if (c < tab_base || c >= tab_base + 64) {
-      tab_base = c;
-      const int cc = c + lane_id();
-      tab = (cc <= chi) ? trow[cc] : 0;
-    }
     int blk = __builtin_amdgcn_readlane(tab, c - tab_base);
-    if (blk < 0 || static_cast<int64_t>(blk) >= nb) {
+    if (blk < 0 || blk >= nb32) {
       bad = true;
       blk = 0;
     }
@@ -173,47 +217,75 @@ struct Item {
 
   __device__ __forceinline__ int clampc(int c) const { return min(max(c, clo), chi); }
 
+  // K/V loads go through buffer resources built per tile in SGPRs: the lane
+  // offsets are loop-invariant 32-bit VGPRs, so issuing a stage writes no
+  // vector registers besides the load destinations, and the hardware range
+  // check of the resource keeps every access inside its tile.
   __device__ __forceinline__ void issue(Stage& st, int t32) {
     const int lane = lane_id();
     const int m = lane & 15, q = lane >> 4;
     const int base = t32 * kSub;
-    // ---- K: pair row m of the sub-tile = tokens base+2m, base+2m+1
-    const uint8_t* kp;
-    const uint8_t* vp;
+    const uint32_t koff = static_cast<uint32_t>((m & 7) * (2 * kHeadDim) + 32 * q);
     if constexpr (BK >= kSub) {
-      const int c = clampc(base / BK);
-      const int blk = block_of(c);
+      const int blk = block_of(clampc(base / BK));
       const int64_t tile = (static_cast<int64_t>(blk) * hkv + h) * (BK * kHeadDim);
-      const int tb = base % BK;
-      kp = kbase + tile + (tb / 2 + m) * (2 * kHeadDim) + 32 * q;
-      vp = vbase + tile + (tb + 8 * q) * kHeadDim + 4 * m;
+      const rsrc_t rk = tile_rsrc(kbase + tile, BK * kHeadDim);
+      const rsrc_t rv = tile_rsrc(vbase + tile, BK * kHeadDim);
+      const int so = (base % BK) * kHeadDim;
+      const uint32_t kof = static_cast<uint32_t>(m * (2 * kHeadDim) + 32 * q);
+      const uint32_t vof = static_cast<uint32_t>(8 * q * kHeadDim + 4 * m);
+      st.k0 = __builtin_amdgcn_raw_buffer_load_b128(rk, kof, so, 0);
+      st.k1 = __builtin_amdgcn_raw_buffer_load_b128(rk, kof + 16, so, 0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        st.v[i] = __builtin_amdgcn_raw_buffer_load_b32(rv, vof, so + i * kHeadDim, 0);
     } else {
-      // BK == 16: the sub-tile spans two blocks
+      // BK == 16: the sub-tile spans two blocks; pair rows 0-7 and tokens
+      // 0-15 come from the first, the rest from the second
       const int c0 = clampc(base / BK), c1 = clampc(base / BK + 1);
       const int blk0 = block_of(c0), blk1 = block_of(c1);
-      const int blk_k = (m < 8) ? blk0 : blk1;
-      const int blk_v = (q < 2) ? blk0 : blk1;
-      const int64_t tk = (static_cast<int64_t>(blk_k) * hkv + h) * (BK * kHeadDim);
-      const int64_t tv = (static_cast<int64_t>(blk_v) * hkv + h) * (BK * kHeadDim);
-      kp = kbase + tk + (m & 7) * (2 * kHeadDim) + 32 * q;
-      vp = vbase + tv + ((8 * q) & 15) * kHeadDim + 4 * m;
-    }
-    st.k0 = *reinterpret_cast<const u32x4_t*>(kp);
-    st.k1 = *reinterpret_cast<const u32x4_t*>(kp + 16);
+      const int64_t t0 = (static_cast<int64_t>(blk0) * hkv + h) * (BK * kHeadDim);
+      const int64_t t1 = (static_cast<int64_t>(blk1) * hkv + h) * (BK * kHeadDim);
+      const rsrc_t rk = tile_rsrc(kbase + (m < 8 ? t0 : t1), BK * kHeadDim);
+      const rsrc_t rv = tile_rsrc(vbase + (q < 2 ? t0 : t1), BK * kHeadDim);
+      const uint32_t vof = static_cast<uint32_t>(((8 * q) & 15) * kHeadDim + 4 * m);
+      if (m < 8) {
+        st.k0 = __builtin_amdgcn_raw_buffer_load_b128(tile_rsrc(kbase + t0, BK * kHeadDim), koff, 0, 0);
+        st.k1 = __builtin_amdgcn_raw_buffer_load_b128(tile_rsrc(kbase + t0, BK * kHeadDim), koff + 16, 0, 0);
+      } else {
+        st.k0 = __builtin_amdgcn_raw_buffer_load_b128(tile_rsrc(kbase + t1, BK * kHeadDim), koff, 0, 0);
+        st.k1 = __builtin_amdgcn_raw_buffer_load_b128(tile_rsrc(kbase + t1, BK * kHeadDim), koff + 16, 0, 0);
+      }
+      if (q < 2) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) st.v[i] = *reinterpret_cast<const uint32_t*>(vp + i * kHeadDim);
+        for (int i = 0; i < 8; ++i)
+          st.v[i] = __builtin_amdgcn_raw_buffer_load_b32(tile_rsrc(vbase + t0, BK * kHeadDim), vof + i * kHeadDim, 0, 0);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          st.v[i] = __builtin_amdgcn_raw_buffer_load_b32(tile_rsrc(vbase + t1, BK * kHeadDim), vof + i * kHeadDim, 0, 0);
+      }
+      (void)rk;
+      (void)rv;
+    }
   }
 };
 
-template <int BK, bool WINDOWED>
-__device__ __forceinline__ void compute_subtile(const AttnArgs& a, Stage& st, int t32, int lo,
-                                                int hi, const uint32_t (&qx)[4][4], State& s) {
+// One 32-token sub-tile: scores, online-softmax update and PV accumulation.
+// MASKED selects the edge path (keys outside [lo, hi] removed); the stage
+// registers are never written here, so the interior path carries no copies.
+template <bool MASKED>
+__device__ __forceinline__ void compute_subtile(const Stage& st, int t32, int lo, int hi,
+                                                float score_scale, const uint32_t (&qx)[4][4],
+                                                State& s) {
   const int lane = lane_id();
   const int m = lane & 15, q = lane >> 4, e = m >> 3;
   const int base = t32 * kSub;
-  const bool interior = (base >= lo) && (base + kSub - 1 <= hi);
   uint32_t kd[8] = {st.k0[0], st.k0[1], st.k0[2], st.k0[3], st.k1[0], st.k1[1], st.k1[2], st.k1[3]};
-  if (!interior) {
+  uint32_t vd[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) vd[i] = st.v[i];
+  if constexpr (MASKED) {
     // zero the bytes of out-of-range tokens so 0 * NaN never reaches a score
     const int t_even = base + 2 * m;
     const bool ok0 = (t_even >= lo) && (t_even <= hi);
@@ -224,7 +296,7 @@ __device__ __forceinline__ void compute_subtile(const AttnArgs& a, Stage& st, in
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int t = base + 8 * q + i;
-      if (t < lo || t > hi) st.v[i] = 0u;
+      vd[i] = (t < lo || t > hi) ? 0u : vd[i];
     }
   }
   // ---- S^T = Kp * Qx
@@ -241,8 +313,8 @@ __device__ __forceinline__ void compute_subtile(const AttnArgs& a, Stage& st, in
   float x[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    x[r] = sacc[r] * a.score_scale;
-    if (!interior) {
+    x[r] = sacc[r] * score_scale;
+    if constexpr (MASKED) {
       const int t = base + 8 * q + 2 * r + e;
       if (t < lo || t > hi) x[r] = -INFINITY;
     }
@@ -269,8 +341,8 @@ __device__ __forceinline__ void compute_subtile(const AttnArgs& a, Stage& st, in
   uint32_t vop[4][4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const uint32_t lo2 = __builtin_amdgcn_perm(st.v[2 * k + 1], st.v[2 * k], 0x05010400u);
-    const uint32_t hi2 = __builtin_amdgcn_perm(st.v[2 * k + 1], st.v[2 * k], 0x07030602u);
+    const uint32_t lo2 = __builtin_amdgcn_perm(vd[2 * k + 1], vd[2 * k], 0x05010400u);
+    const uint32_t hi2 = __builtin_amdgcn_perm(vd[2 * k + 1], vd[2 * k], 0x07030602u);
     vop[0][k] = e4m3x2_to_f16x2<false>(lo2);
     vop[1][k] = e4m3x2_to_f16x2<true>(lo2);
     vop[2][k] = e4m3x2_to_f16x2<false>(hi2);
@@ -296,43 +368,17 @@ __device__ __forceinline__ void store_bf16x16(uint16_t* dst, const float* v) {
 
 constexpr int kSlotFloats = 8 * kHeadDim + 16;  // o[8][64], m[8], l[8]
 
+// Process the sub-tiles [cur, wend) of the item line: chunk `wid` of size
+// `chunk`.  Items that lie wholly inside are written out; pieces of items cut
+// by chunk boundaries go through partial slots 2*wid (head) / 2*wid+1 (tail)
+// and are merged by the last piece to arrive.
 template <int BK, bool WINDOWED>
-__global__ void __launch_bounds__(256, kWGPerCU) decode_attn_kernel(AttnArgs a) {
-  extern __shared__ int s_pre[];  // [B + 1] prefix of per-sequence sub-tile counts
-  const int tid = threadIdx.x;
-  const int B = a.B;
-  for (int b = tid; b < B; b += 256) {
-    int lo = 0;
-    bool inv;
-    s_pre[b] = seq_subtiles<BK, WINDOWED>(a, a.frame_pos[b], &lo, &inv);
-  }
-  __syncthreads();
-  block_exclusive_scan(s_pre, B);
-
-  // rows with no work: +0 for inactive sequences, NaN for invalid positions
-  for (int b = blockIdx.x; b < B; b += gridDim.x) {
-    if (s_pre[b + 1] != s_pre[b]) continue;
-    int lo = 0;
-    bool inv;
-    seq_subtiles<BK, WINDOWED>(a, a.frame_pos[b], &lo, &inv);
-    const uint16_t fill = inv ? 0x7fc0u : 0u;
-    const uint32_t f2 = static_cast<uint32_t>(fill) * 0x10001u;
-    u32x4_t* row = reinterpret_cast<u32x4_t*>(a.out + static_cast<int64_t>(b) * a.Hq * kHeadDim);
-    for (int i = tid; i < a.Hq * kHeadDim / 8; i += 256) row[i] = u32x4_t{f2, f2, f2, f2};
-  }
-
-  const int lane = tid & 63;
+__device__ __forceinline__ void process_chunk(const AttnArgs& a, const int* s_pre, int B, int wid,
+                                              int64_t chunk, int64_t cur, int64_t wend) {
+  const int lane = lane_id();
   const int m = lane & 15, q = lane >> 4, e = m >> 3, g = m & 7;
-  const int wid = blockIdx.x * kWavesPerWG + (tid >> 6);
-  const int64_t total = static_cast<int64_t>(s_pre[B]) * a.Hkv;
-  if (total == 0) return;
-  const int64_t chunk = (total + a.n_workers - 1) / a.n_workers;
-  int64_t cur = static_cast<int64_t>(wid) * chunk;
-  const int64_t wend = min(cur + chunk, total);
-  if (cur >= wend) return;
   const int64_t wbeg = cur;
-
-  // locate the first item: the last b with s_pre[b] * Hkv <= cur
+  // locate the first item: the last b with s_pre[b] * Hkv <= cur (uniform)
   int b;
   {
     int lo_i = 0, hi_i = B - 1;
@@ -342,17 +388,19 @@ __global__ void __launch_bounds__(256, kWGPerCU) decode_attn_kernel(AttnArgs a) 
     }
     b = lo_i;
   }
+  b = __builtin_amdgcn_readfirstlane(b);
   int n = s_pre[b + 1] - s_pre[b];
   int64_t rel = cur - static_cast<int64_t>(s_pre[b]) * a.Hkv;
-  int h = static_cast<int>(rel / n);
-  int j = static_cast<int>(rel % n);
+  int h = __builtin_amdgcn_readfirstlane(static_cast<int>(rel / n));
+  int j = __builtin_amdgcn_readfirstlane(static_cast<int>(rel % n));
 
   while (cur < wend && b < B) {
-    n = s_pre[b + 1] - s_pre[b];
+    n = __builtin_amdgcn_readfirstlane(s_pre[b + 1] - s_pre[b]);
+    const int pre_b = __builtin_amdgcn_readfirstlane(s_pre[b]);
     const int seg = static_cast<int>(min(static_cast<int64_t>(n - j), wend - cur));
-    const int64_t item_beg = static_cast<int64_t>(s_pre[b]) * a.Hkv + static_cast<int64_t>(h) * n;
+    const int64_t item_beg = static_cast<int64_t>(pre_b) * a.Hkv + static_cast<int64_t>(h) * n;
     const int64_t item_end = item_beg + n;
-    const int hi = a.frame_pos[b];
+    const int hi = __builtin_amdgcn_readfirstlane(a.frame_pos[b]);
     const int lo = WINDOWED ? max(0, hi - a.window + 1) : 0;
 
     // expanded queries: qx[i][k] holds q[g][16q + 4i + k] in the half of parity e
@@ -385,15 +433,30 @@ __global__ void __launch_bounds__(256, kWGPerCU) decode_attn_kernel(AttnArgs a) 
     const int t0 = lo / kSub + j;
     const int tlast = t0 + seg - 1;
 
-    // two-stage software pipeline over the segment's sub-tiles
-    Stage sa, sb;
-    it.issue(sa, t0);
-    for (int i = 0; i < seg; i += 2) {
-      it.issue(sb, min(t0 + i + 1, tlast));
-      compute_subtile<BK, WINDOWED>(a, sa, t0 + i, lo, hi, qx, s);
-      if (i + 1 >= seg) break;
-      it.issue(sa, min(t0 + i + 2, tlast));
-      compute_subtile<BK, WINDOWED>(a, sb, t0 + i + 1, lo, hi, qx, s);
+    // Two-stage software pipeline over the segment's sub-tiles, run per
+    // window of 64 table entries.
+    for (int tw = t0; tw <= tlast;) {
+      const int cw0 = it.clampc((tw * kSub) / BK);
+      it.load_window(cw0);
+      const int twl = min(tlast, ((cw0 + 64) * BK) / kSub - 1);
+      // kDepth stages in flight: stage d holds sub-tile i + d; each stage is
+      // refilled right after it has been consumed
+      Stage st[kDepth];
+#pragma unroll
+      for (int d = 0; d < kDepth; ++d) it.issue(st[d], min(tw + d, twl));
+      for (int i = tw; i <= twl; i += kDepth) {
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) {
+          if (i + d > twl) break;
+          const int t32 = i + d;
+          if (t32 * kSub >= lo && t32 * kSub + kSub - 1 <= hi)
+            compute_subtile<false>(st[d], t32, lo, hi, a.score_scale, qx, s);
+          else
+            compute_subtile<true>(st[d], t32, lo, hi, a.score_scale, qx, s);
+          it.issue(st[d], min(i + d + kDepth, twl));
+        }
+      }
+      tw = twl + 1;
     }
     s.bad = it.bad;
 
@@ -424,28 +487,28 @@ __global__ void __launch_bounds__(256, kWGPerCU) decode_attn_kernel(AttnArgs a) 
       const int slot = (item_beg >= wbeg) ? 2 * wid + 1 : 2 * wid;
       float* ps = a.partial + static_cast<int64_t>(slot) * kSlotFloats;
       if (e == 0) {
-        f32x4_t* po = reinterpret_cast<f32x4_t*>(ps + g * kHeadDim + 16 * q);
+        float* po = ps + g * kHeadDim + 16 * q;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) po[i] = f32x4_t{o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
+        for (int i = 0; i < 16; ++i) st_coherent(po + i, o[i]);
         if (q == 0) {
-          ps[8 * kHeadDim + g] = s.m;
-          ps[8 * kHeadDim + 8 + g] = bad ? NAN : lsum;
+          st_coherent(ps + 8 * kHeadDim + g, s.m);
+          st_coherent(ps + 8 * kHeadDim + 8 + g, bad ? NAN : lsum);
         }
       }
-      __threadfence();
+      wait_vm_stores();
       int old = 0;
       int32_t* ctr = a.counters + static_cast<int64_t>(b) * a.Hkv + h;
-      if (lane == 0) old = atomicAdd(ctr, 1);
+      if (lane == 0) old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       old = __shfl(old, 0, 64);
       const int ncontrib = static_cast<int>(wlast - wfirst + 1);
       if (old == ncontrib - 1) {
-        __threadfence();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
         // merge every piece of the item: first worker's tail slot, then the
         // head slots of the following workers
         float mm = -INFINITY;
         for (int k = 0; k < ncontrib; ++k) {
           const int sl = (k == 0) ? static_cast<int>(2 * wfirst + 1) : static_cast<int>(2 * (wfirst + k));
-          mm = fmaxf(mm, __builtin_nontemporal_load(a.partial + static_cast<int64_t>(sl) * kSlotFloats + 8 * kHeadDim + g));
+          mm = fmaxf(mm, ld_coherent(a.partial + static_cast<int64_t>(sl) * kSlotFloats + 8 * kHeadDim + g));
         }
         float acc[16];
 #pragma unroll
@@ -454,14 +517,13 @@ __global__ void __launch_bounds__(256, kWGPerCU) decode_attn_kernel(AttnArgs a) 
         for (int k = 0; k < ncontrib; ++k) {
           const int sl = (k == 0) ? static_cast<int>(2 * wfirst + 1) : static_cast<int>(2 * (wfirst + k));
           const float* pk = a.partial + static_cast<int64_t>(sl) * kSlotFloats;
-          const float mk = __builtin_nontemporal_load(pk + 8 * kHeadDim + g);
-          const float lk = __builtin_nontemporal_load(pk + 8 * kHeadDim + 8 + g);
+          const float mk = ld_coherent(pk + 8 * kHeadDim + g);
+          const float lk = ld_coherent(pk + 8 * kHeadDim + 8 + g);
           const float w = __builtin_amdgcn_exp2f(mk - mm);
           ltot += w * lk;
           if (e == 0) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-              acc[i] += w * __builtin_nontemporal_load(pk + g * kHeadDim + 16 * q + i);
+            for (int i = 0; i < 16; ++i) acc[i] += w * ld_coherent(pk + g * kHeadDim + 16 * q + i);
           }
         }
         if (e == 0 && g < a.G) {
@@ -470,7 +532,7 @@ __global__ void __launch_bounds__(256, kWGPerCU) decode_attn_kernel(AttnArgs a) 
           for (int i = 0; i < 16; ++i) acc[i] *= f;
           store_bf16x16(a.out + (static_cast<int64_t>(b) * a.Hq + h * a.G + g) * kHeadDim + 16 * q, acc);
         }
-        if (lane == 0) *ctr = 0;
+        if (lane == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
 
@@ -481,13 +543,50 @@ __global__ void __launch_bounds__(256, kWGPerCU) decode_attn_kernel(AttnArgs a) 
       do {
         ++b;
       } while (b < B && s_pre[b + 1] == s_pre[b]);
+      b = __builtin_amdgcn_readfirstlane(b);
     }
   }
 }
 
 template <int BK, bool WINDOWED>
+__global__ void __launch_bounds__(kThreads, kWGPerCU * kWavesPerWG / 4) decode_attn_kernel(AttnArgs a) {
+  extern __shared__ int s_pre[];  // [B + 1] prefix of per-sequence sub-tile counts
+  const int tid = threadIdx.x;
+  const int B = a.B;
+  for (int b = tid; b < B; b += kThreads) {
+    int lo = 0;
+    bool inv;
+    s_pre[b] = seq_subtiles<BK, WINDOWED>(a, a.frame_pos[b], &lo, &inv);
+  }
+  __syncthreads();
+  block_exclusive_scan(s_pre, B);
+
+  // rows with no work: +0 for inactive sequences, NaN for invalid positions
+  for (int b = blockIdx.x; b < B; b += gridDim.x) {
+    if (s_pre[b + 1] != s_pre[b]) continue;
+    int lo = 0;
+    bool inv;
+    seq_subtiles<BK, WINDOWED>(a, a.frame_pos[b], &lo, &inv);
+    const uint16_t fill = inv ? 0x7fc0u : 0u;
+    const uint32_t f2 = static_cast<uint32_t>(fill) * 0x10001u;
+    u32x4_t* row = reinterpret_cast<u32x4_t*>(a.out + static_cast<int64_t>(b) * a.Hq * kHeadDim);
+    for (int i = tid; i < a.Hq * kHeadDim / 8; i += kThreads) row[i] = u32x4_t{f2, f2, f2, f2};
+  }
+
+  // Static stream-K split: wave w owns the contiguous sub-tile range
+  // [w*chunk, (w+1)*chunk) of the item line.
+  const int64_t total = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(s_pre[B])) * a.Hkv;
+  if (total == 0) return;
+  const int wid = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerWG + (tid >> 6));
+  const int64_t chunk = (total + a.n_workers - 1) / a.n_workers;
+  const int64_t cb = static_cast<int64_t>(wid) * chunk;
+  if (cb >= total) return;
+  process_chunk<BK, WINDOWED>(a, s_pre, B, wid, chunk, cb, min(cb + chunk, total));
+}
+
+template <int BK, bool WINDOWED>
 hipError_t launch(const AttnArgs& a, int n_wg, size_t lds, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_attn_kernel<BK, WINDOWED>), dim3(n_wg), dim3(256), lds, stream, a);
+  hipLaunchKernelGGL((decode_attn_kernel<BK, WINDOWED>), dim3(n_wg), dim3(kThreads), lds, stream, a);
   return hipGetLastError();
 }
 
@@ -498,7 +597,7 @@ int attn_workers(int64_t batch, int kv_heads, int max_subtiles) {
   int64_t w = (total + kMinSubtilesPerWorker - 1) / kMinSubtilesPerWorker;
   w = (w + kWavesPerWG - 1) / kWavesPerWG * kWavesPerWG;
   if (w < kWavesPerWG) w = kWavesPerWG;
-  if (w > kMaxWorkers) w = kMaxWorkers;
+  if (w > kMaxWorkers) w = kMaxWorkers / kWavesPerWG * kWavesPerWG;
   return static_cast<int>(w);
 }
 
@@ -508,9 +607,16 @@ int attn_max_subtiles(int block, int table_width, int window) {
   return static_cast<int>((keys + kSub - 1) / kSub + 1);
 }
 
+// Workspace layout: [arrival counters, B*Hkv int32][queue, 2 int32][partial
+// slots, 2 per chunk], each region 256-byte aligned.
+static int64_t counters_bytes(int64_t batch, int kv_heads) {
+  return (batch * kv_heads * 4 + 255) / 256 * 256;
+}
+constexpr int64_t kQueueBytes = 256;
+
 int64_t attn_workspace_bytes(int64_t batch, int kv_heads, int n_workers) {
-  const int64_t ctr = (batch * kv_heads * 4 + 255) / 256 * 256;
-  return ctr + static_cast<int64_t>(2) * n_workers * kSlotFloats * 4;
+  return counters_bytes(batch, kv_heads) + kQueueBytes +
+         static_cast<int64_t>(2) * kChunksPerWorker * n_workers * kSlotFloats * 4;
 }
 
 hipError_t launch_decode_attn(const AttnLaunch& L, hipStream_t stream) {
@@ -521,9 +627,10 @@ hipError_t launch_decode_attn(const AttnLaunch& L, hipStream_t stream) {
   a.table = L.table;
   a.frame_pos = L.frame_pos;
   a.out = L.out;
-  const int64_t ctr = (static_cast<int64_t>(L.B) * L.Hkv * 4 + 255) / 256 * 256;
+  const int64_t ctr = counters_bytes(L.B, L.Hkv);
   a.counters = reinterpret_cast<int32_t*>(L.workspace);
-  a.partial = reinterpret_cast<float*>(reinterpret_cast<char*>(L.workspace) + ctr);
+  a.queue = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(L.workspace) + ctr);
+  a.partial = reinterpret_cast<float*>(reinterpret_cast<char*>(L.workspace) + ctr + kQueueBytes);
   a.nb = L.nb;
   a.B = L.B;
   a.Hq = L.Hq;
