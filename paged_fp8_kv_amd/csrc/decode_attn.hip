@@ -52,6 +52,7 @@ constexpr float kRescaleSlack = 8.0f; // log2 units
 constexpr int kDepth = PKV_DEPTH;     // sub-tiles in flight per wave
 constexpr int kChunksPerWorker = 2;   // chunks of the item line per wave, on average
 constexpr int kMinChunk = 8;          // sub-tiles
+constexpr int kTinyItem = 8;          // items this short (sub-tiles) are never split
 // Waves per SIMD the kernel is compiled for (= workgroups per CU, 4 waves
 // each); the stream-K shares assume every worker is resident at once.
 #ifndef PKV_WG_PER_CU
@@ -368,6 +369,25 @@ __device__ __forceinline__ void store_bf16x16(uint16_t* dst, const float* v) {
 
 constexpr int kSlotFloats = 8 * kHeadDim + 16;  // o[8][64], m[8], l[8]
 
+// Offset (in the item line) of the first item that starts at or after x;
+// `total` when there is none.  Items are (b, h) in order, sequence b holding
+// Hkv items of s_pre[b+1]-s_pre[b] sub-tiles each.
+__device__ __forceinline__ int64_t first_item_start_at_or_after(const int* s_pre, int B, int hkv,
+                                                                int64_t x) {
+  const int64_t total = static_cast<int64_t>(s_pre[B]) * hkv;
+  if (x >= total) return total;
+  int lo_i = 0, hi_i = B - 1;  // last b with s_pre[b] * hkv <= x
+  while (lo_i < hi_i) {
+    const int mid = (lo_i + hi_i + 1) >> 1;
+    if (static_cast<int64_t>(s_pre[mid]) * hkv <= x) lo_i = mid; else hi_i = mid - 1;
+  }
+  const int64_t base = static_cast<int64_t>(s_pre[lo_i]) * hkv;
+  const int n = s_pre[lo_i + 1] - s_pre[lo_i];
+  const int64_t h = (x - base + n - 1) / n;  // first item of b at or after x
+  if (h < hkv) return base + h * n;
+  return static_cast<int64_t>(s_pre[lo_i + 1]) * hkv;  // first item of the next sequence with work
+}
+
 // Process the sub-tiles [cur, wend) of the item line: chunk `wid` of size
 // `chunk`.  Items that lie wholly inside are written out; pieces of items cut
 // by chunk boundaries go through partial slots 2*wid (head) / 2*wid+1 (tail)
@@ -551,13 +571,20 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const int* s_pr
 template <int BK, bool WINDOWED>
 __global__ void __launch_bounds__(kThreads, kWGPerCU * kWavesPerWG / 4) decode_attn_kernel(AttnArgs a) {
   extern __shared__ int s_pre[];  // [B + 1] prefix of per-sequence sub-tile counts
+  __shared__ int s_longest;       // longest item, in sub-tiles
   const int tid = threadIdx.x;
   const int B = a.B;
+  if (tid == 0) s_longest = 0;
+  __syncthreads();
+  int longest = 0;
   for (int b = tid; b < B; b += kThreads) {
     int lo = 0;
     bool inv;
-    s_pre[b] = seq_subtiles<BK, WINDOWED>(a, a.frame_pos[b], &lo, &inv);
+    const int n = seq_subtiles<BK, WINDOWED>(a, a.frame_pos[b], &lo, &inv);
+    s_pre[b] = n;
+    longest = max(longest, n);
   }
+  atomicMax(&s_longest, longest);
   __syncthreads();
   block_exclusive_scan(s_pre, B);
 
@@ -573,15 +600,25 @@ __global__ void __launch_bounds__(kThreads, kWGPerCU * kWavesPerWG / 4) decode_a
     for (int i = tid; i < a.Hq * kHeadDim / 8; i += kThreads) row[i] = u32x4_t{f2, f2, f2, f2};
   }
 
-  // Static stream-K split: wave w owns the contiguous sub-tile range
-  // [w*chunk, (w+1)*chunk) of the item line.
+  // Static split of the item line over the waves.  Wave w's share is the
+  // sub-tile range [w*chunk, (w+1)*chunk).  Short items are never cut: when
+  // every item is tiny or at most half a share, wave w takes the whole items
+  // whose first sub-tile falls in its share (no partials, no merge); otherwise
+  // shares are exact and cut items are merged through the workspace.
   const int64_t total = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(s_pre[B])) * a.Hkv;
   if (total == 0) return;
   const int wid = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerWG + (tid >> 6));
   const int64_t chunk = (total + a.n_workers - 1) / a.n_workers;
   const int64_t cb = static_cast<int64_t>(wid) * chunk;
   if (cb >= total) return;
-  process_chunk<BK, WINDOWED>(a, s_pre, B, wid, chunk, cb, min(cb + chunk, total));
+  const int longest_item = __builtin_amdgcn_readfirstlane(s_longest);
+  if (longest_item <= kTinyItem || 2 * static_cast<int64_t>(longest_item) <= chunk) {
+    const int64_t lo_w = first_item_start_at_or_after(s_pre, B, a.Hkv, cb);
+    const int64_t hi_w = first_item_start_at_or_after(s_pre, B, a.Hkv, min(cb + chunk, total));
+    if (lo_w < hi_w) process_chunk<BK, WINDOWED>(a, s_pre, B, wid, chunk, lo_w, hi_w);
+  } else {
+    process_chunk<BK, WINDOWED>(a, s_pre, B, wid, chunk, cb, min(cb + chunk, total));
+  }
 }
 
 template <int BK, bool WINDOWED>
