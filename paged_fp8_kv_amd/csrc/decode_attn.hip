@@ -174,6 +174,76 @@ struct Stage {
   uint32_t v[8];    // V dwords: tokens 8q..8q+7, dims 4m..4m+3
 };
 
+// ---- LDS staging of K/V sub-tiles ------------------------------------------
+// Each wave owns a ring of kDepth slots of 4 KiB (K 2 KiB, V 2 KiB).  A slot is
+// filled by four 1 KiB direct-to-LDS buffer loads (16 bytes per lane, whole
+// 128-byte lines per instruction); lane L's 16 bytes land at slot + 16*L.  The
+// global chunk each lane fetches is chosen so that the slot holds a swizzled
+// image from which the MFMA operands are read without bank conflicts:
+//  * K: pair row r (128 B = 8 chunks) keeps chunk c at position
+//    8r + (c ^ fk(r)), fk(r) = (r & 7) ^ (r >> 3);
+//  * V: token t (64 B = 4 chunks) sits in row slot
+//    s(t) = (t & ~3) | ((t + (t >> 3)) & 3), so the four tokens 8q+i read
+//    together by the four lane groups fall in different banks.
+constexpr int kSlotBytes = 4096;
+typedef __attribute__((address_space(3))) uint8_t* lds_ptr_t;
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource of `bytes` bytes at p, as four SGPRs.
+__device__ __forceinline__ i32x4_t tile_desc(const uint8_t* p, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  return i32x4_t{static_cast<int32_t>(static_cast<uint32_t>(a)),
+                 static_cast<int32_t>(static_cast<uint32_t>(a >> 32) & 0xffffu), bytes, kRsrcWord3};
+}
+
+// One 16-byte-per-lane load from a buffer resource into LDS at
+// lds_addr + 16 * lane.  Issued as inline assembly on purpose: the compiler
+// cannot tell ring slots apart and would otherwise drain every outstanding
+// direct-to-LDS load before each LDS read.  Completion is tracked by the
+// explicit vmcnt waits below; the compiler's own waits for other loads only
+// become stricter.
+__device__ __forceinline__ void dma16(i32x4_t desc, uint32_t voff, uint32_t soff,
+                                      uint32_t lds_addr) {
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(desc), "s"(soff), "{m0}"(lds_addr)
+               : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr_of(const uint8_t* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)(const_cast<uint8_t*>(p))));
+}
+
+__device__ __forceinline__ int fk_swz(int r) { return (r & 7) ^ (r >> 3); }
+__device__ __forceinline__ int v_row_slot(int t) { return (t & ~3) | ((t + (t >> 3)) & 3); }
+__device__ __forceinline__ int v_row_token(int s) { return (s & ~3) | ((s - (s >> 3)) & 3); }
+
+// s_waitcnt vmcnt(N) (expcnt / lgkmcnt left alone), fenced against compiler
+// reordering of LDS accesses: direct-to-LDS loads are not tracked by the
+// compiler's own wait insertion, so every read of a slot follows one of these.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Wait until at most n sub-tiles' loads (four instructions each) are
+// outstanding, 0 <= n < kDepth.
+__device__ __forceinline__ void wait_vmcnt_slots(int n) {
+  static_assert(kDepth <= 8, "wait table below");
+  switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<4>(); break;
+    case 2: wait_vmcnt<8>(); break;
+    case 3: wait_vmcnt<12>(); break;
+    case 4: wait_vmcnt<16>(); break;
+    case 5: wait_vmcnt<20>(); break;
+    case 6: wait_vmcnt<24>(); break;
+    default: wait_vmcnt<28>(); break;
+  }
+}
+
 template <int BK, bool WINDOWED>
 struct Item {
   const uint8_t* kbase;
@@ -218,59 +288,64 @@ struct Item {
 
   __device__ __forceinline__ int clampc(int c) const { return min(max(c, clo), chi); }
 
-  // K/V loads go through buffer resources built per tile in SGPRs: the lane
-  // offsets are loop-invariant 32-bit VGPRs, so issuing a stage writes no
-  // vector registers besides the load destinations, and the hardware range
-  // check of the resource keeps every access inside its tile.
-  __device__ __forceinline__ void issue(Stage& st, int t32) {
+  // Fill ring slot `slot` with sub-tile t32 (four direct-to-LDS loads through
+  // per-tile buffer resources; the resource range check keeps every access
+  // inside its tile).
+  __device__ __forceinline__ void issue(uint8_t* ring, int slot, int t32) {
     const int lane = lane_id();
-    const int m = lane & 15, q = lane >> 4;
     const int base = t32 * kSub;
-    const uint32_t koff = static_cast<uint32_t>((m & 7) * (2 * kHeadDim) + 32 * q);
+    const uint32_t dst = lds_addr_of(ring + slot * kSlotBytes);
     if constexpr (BK >= kSub) {
       const int blk = block_of(clampc(base / BK));
       const int64_t tile = (static_cast<int64_t>(blk) * hkv + h) * (BK * kHeadDim);
-      const rsrc_t rk = tile_rsrc(kbase + tile, BK * kHeadDim);
-      const rsrc_t rv = tile_rsrc(vbase + tile, BK * kHeadDim);
-      const int so = (base % BK) * kHeadDim;
-      const uint32_t kof = static_cast<uint32_t>(m * (2 * kHeadDim) + 32 * q);
-      const uint32_t vof = static_cast<uint32_t>(8 * q * kHeadDim + 4 * m);
-      st.k0 = __builtin_amdgcn_raw_buffer_load_b128(rk, kof, so, 0);
-      st.k1 = __builtin_amdgcn_raw_buffer_load_b128(rk, kof + 16, so, 0);
+      const i32x4_t rk = tile_desc(kbase + tile, BK * kHeadDim);
+      const i32x4_t rv = tile_desc(vbase + tile, BK * kHeadDim);
+      const uint32_t so = static_cast<uint32_t>((base % BK) * kHeadDim);
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        st.v[i] = __builtin_amdgcn_raw_buffer_load_b32(rv, vof, so + i * kHeadDim, 0);
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t kof = static_cast<uint32_t>((8 * j + (lane >> 3)) * 128 +
+                                                   (((lane & 7) ^ (lane >> 3) ^ j) * 16));
+        dma16(rk, kof, so, dst + 1024 * j);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int t = v_row_token(16 * j + (lane >> 2));
+        const uint32_t vof = static_cast<uint32_t>(t * kHeadDim + (lane & 3) * 16);
+        dma16(rv, vof, so, dst + 2048 + 1024 * j);
+      }
     } else {
-      // BK == 16: the sub-tile spans two blocks; pair rows 0-7 and tokens
-      // 0-15 come from the first, the rest from the second
-      const int c0 = clampc(base / BK), c1 = clampc(base / BK + 1);
-      const int blk0 = block_of(c0), blk1 = block_of(c1);
-      const int64_t t0 = (static_cast<int64_t>(blk0) * hkv + h) * (BK * kHeadDim);
-      const int64_t t1 = (static_cast<int64_t>(blk1) * hkv + h) * (BK * kHeadDim);
-      const rsrc_t rk = tile_rsrc(kbase + (m < 8 ? t0 : t1), BK * kHeadDim);
-      const rsrc_t rv = tile_rsrc(vbase + (q < 2 ? t0 : t1), BK * kHeadDim);
-      const uint32_t vof = static_cast<uint32_t>(((8 * q) & 15) * kHeadDim + 4 * m);
-      if (m < 8) {
-        st.k0 = __builtin_amdgcn_raw_buffer_load_b128(tile_rsrc(kbase + t0, BK * kHeadDim), koff, 0, 0);
-        st.k1 = __builtin_amdgcn_raw_buffer_load_b128(tile_rsrc(kbase + t0, BK * kHeadDim), koff + 16, 0, 0);
-      } else {
-        st.k0 = __builtin_amdgcn_raw_buffer_load_b128(tile_rsrc(kbase + t1, BK * kHeadDim), koff, 0, 0);
-        st.k1 = __builtin_amdgcn_raw_buffer_load_b128(tile_rsrc(kbase + t1, BK * kHeadDim), koff + 16, 0, 0);
-      }
-      if (q < 2) {
+      // BK == 16: each load instruction covers one of the two blocks of the
+      // sub-tile (K pair rows 8j.., V tokens 16j..)
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          st.v[i] = __builtin_amdgcn_raw_buffer_load_b32(tile_rsrc(vbase + t0, BK * kHeadDim), vof + i * kHeadDim, 0, 0);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          st.v[i] = __builtin_amdgcn_raw_buffer_load_b32(tile_rsrc(vbase + t1, BK * kHeadDim), vof + i * kHeadDim, 0, 0);
+      for (int j = 0; j < 2; ++j) {
+        const int blk = block_of(clampc(base / BK + j));
+        const int64_t tile = (static_cast<int64_t>(blk) * hkv + h) * (BK * kHeadDim);
+        const i32x4_t rk = tile_desc(kbase + tile, BK * kHeadDim);
+        const i32x4_t rv = tile_desc(vbase + tile, BK * kHeadDim);
+        const uint32_t kof = static_cast<uint32_t>((lane >> 3) * 128 + (((lane & 7) ^ (lane >> 3) ^ j) * 16));
+        dma16(rk, kof, 0u, dst + 1024 * j);
+        const int t = v_row_token(16 * j + (lane >> 2)) - 16 * j;
+        const uint32_t vof = static_cast<uint32_t>(t * kHeadDim + (lane & 3) * 16);
+        dma16(rv, vof, 0u, dst + 2048 + 1024 * j);
       }
-      (void)rk;
-      (void)rv;
     }
   }
 };
+
+// Read a filled slot into the MFMA lane layout: K pair row m, bytes
+// [32q, 32q+32); V dwords of tokens 8q..8q+7 at dims 4m..4m+3.
+__device__ __forceinline__ void read_slot(const uint8_t* ring, int slot, Stage& st) {
+  const int lane = lane_id();
+  const int m = lane & 15, q = lane >> 4;
+  const uint8_t* src = ring + slot * kSlotBytes;
+  const int fk = fk_swz(m);
+  st.k0 = *reinterpret_cast<const u32x4_t*>(src + (8 * m + ((2 * q) ^ fk)) * 16);
+  st.k1 = *reinterpret_cast<const u32x4_t*>(src + (8 * m + ((2 * q + 1) ^ fk)) * 16);
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    st.v[i] = *reinterpret_cast<const uint32_t*>(src + 2048 + v_row_slot(8 * q + i) * kHeadDim +
+                                                 (m >> 2) * 16 + (m & 3) * 4);
+}
 
 // One 32-token sub-tile: scores, online-softmax update and PV accumulation.
 // MASKED selects the edge path (keys outside [lo, hi] removed); the stage
@@ -394,7 +469,8 @@ __device__ __forceinline__ int64_t first_item_start_at_or_after(const int* s_pre
 // and are merged by the last piece to arrive.
 template <int BK, bool WINDOWED>
 __device__ __forceinline__ void process_chunk(const AttnArgs& a, const int* s_pre, int B, int wid,
-                                              int64_t chunk, int64_t cur, int64_t wend) {
+                                              int64_t chunk, int64_t cur, int64_t wend,
+                                              uint8_t* ring) {
   const int lane = lane_id();
   const int m = lane & 15, q = lane >> 4, e = m >> 3, g = m & 7;
   const int64_t wbeg = cur;
@@ -455,25 +531,42 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const int* s_pr
 
     // Two-stage software pipeline over the segment's sub-tiles, run per
     // window of 64 table entries.
+    // The first run of a segment is shortened by a per-wave amount so that the
+    // waves of a workgroup reach their run boundaries (where the ring drains
+    // and refills) at different times and cover each other's bubbles.
+    int span = __builtin_amdgcn_readfirstlane(64 - 16 * ((threadIdx.x >> 6) & 3));
     for (int tw = t0; tw <= tlast;) {
       const int cw0 = it.clampc((tw * kSub) / BK);
       it.load_window(cw0);
-      const int twl = min(tlast, ((cw0 + 64) * BK) / kSub - 1);
-      // kDepth stages in flight: stage d holds sub-tile i + d; each stage is
-      // refilled right after it has been consumed
-      Stage st[kDepth];
+      const int twl = max(tw, min(tlast, ((cw0 + span) * BK) / kSub - 1));
+      span = 64;
+      // Ring of kDepth slots: sub-tile k lives in slot (k - tw) % kDepth.  While
+      // sub-tile k is computed from registers, sub-tile k+1 is read from its
+      // slot into the other register stage and up to kDepth-1 later sub-tiles
+      // are in flight; slot k is refilled once k has been consumed.
+      static_assert(kDepth % 2 == 0, "register stages alternate with the slot index");
 #pragma unroll
-      for (int d = 0; d < kDepth; ++d) it.issue(st[d], min(tw + d, twl));
+      for (int d = 0; d < kDepth; ++d)
+        if (tw + d <= twl) it.issue(ring, d, tw + d);
+      Stage st[2];
+      wait_vmcnt_slots(min(twl - tw, kDepth - 1));
+      read_slot(ring, 0, st[0]);
       for (int i = tw; i <= twl; i += kDepth) {
 #pragma unroll
         for (int d = 0; d < kDepth; ++d) {
-          if (i + d > twl) break;
           const int t32 = i + d;
+          if (t32 > twl) break;
+          // sub-tile t32+1 is complete once at most the sub-tiles issued after
+          // it (t32+2 .. min(twl, t32+kDepth-1)) are outstanding
+          if (t32 < twl) {
+            wait_vmcnt_slots(min(twl - t32 - 1, kDepth - 2));
+            read_slot(ring, (d + 1) % kDepth, st[(d + 1) & 1]);
+          }
           if (t32 * kSub >= lo && t32 * kSub + kSub - 1 <= hi)
-            compute_subtile<false>(st[d], t32, lo, hi, a.score_scale, qx, s);
+            compute_subtile<false>(st[d & 1], t32, lo, hi, a.score_scale, qx, s);
           else
-            compute_subtile<true>(st[d], t32, lo, hi, a.score_scale, qx, s);
-          it.issue(st[d], min(i + d + kDepth, twl));
+            compute_subtile<true>(st[d & 1], t32, lo, hi, a.score_scale, qx, s);
+          if (t32 + kDepth <= twl) it.issue(ring, d, t32 + kDepth);
         }
       }
       tw = twl + 1;
@@ -572,6 +665,8 @@ template <int BK, bool WINDOWED>
 __global__ void __launch_bounds__(kThreads, kWGPerCU * kWavesPerWG / 4) decode_attn_kernel(AttnArgs a) {
   extern __shared__ int s_pre[];  // [B + 1] prefix of per-sequence sub-tile counts
   __shared__ int s_longest;       // longest item, in sub-tiles
+  __shared__ __attribute__((aligned(16))) uint8_t s_ring[kWavesPerWG * kDepth * kSlotBytes];
+  uint8_t* ring = s_ring + (threadIdx.x >> 6) * (kDepth * kSlotBytes);
   const int tid = threadIdx.x;
   const int B = a.B;
   if (tid == 0) s_longest = 0;
@@ -615,10 +710,11 @@ __global__ void __launch_bounds__(kThreads, kWGPerCU * kWavesPerWG / 4) decode_a
   if (longest_item <= kTinyItem || 2 * static_cast<int64_t>(longest_item) <= chunk) {
     const int64_t lo_w = first_item_start_at_or_after(s_pre, B, a.Hkv, cb);
     const int64_t hi_w = first_item_start_at_or_after(s_pre, B, a.Hkv, min(cb + chunk, total));
-    if (lo_w < hi_w) process_chunk<BK, WINDOWED>(a, s_pre, B, wid, chunk, lo_w, hi_w);
+    if (lo_w < hi_w) process_chunk<BK, WINDOWED>(a, s_pre, B, wid, chunk, lo_w, hi_w, ring);
   } else {
-    process_chunk<BK, WINDOWED>(a, s_pre, B, wid, chunk, cb, min(cb + chunk, total));
+    process_chunk<BK, WINDOWED>(a, s_pre, B, wid, chunk, cb, min(cb + chunk, total), ring);
   }
+  wait_vmcnt<0>();  // no direct-to-LDS load outlives the wave
 }
 
 template <int BK, bool WINDOWED>
