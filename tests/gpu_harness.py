@@ -138,3 +138,38 @@ def assert_close(got_bf16, ref, what=""):
                              f"first {idx.tolist()} got {[g[tuple(i)] for i in idx]} "
                              f"ref {[ref[tuple(i)] for i in idx]}")
     return float(np.max(np.abs(g - ref))) if g.size else 0.0
+
+
+def sampled_blocks(wl, rows):
+    """Sorted ids of every block the given sequences reference (either table)."""
+    ids = np.concatenate([wl.bt_full[rows].ravel(), wl.bt_swa[rows].ravel()])
+    return np.unique(ids[ids >= 0]).astype(np.int64)
+
+
+def gather_blocks(buf, wl, blocks):
+    """Host copy (flat uint8, both halves) of the given blocks of one device
+    buffer, in the order given: block blocks[i] becomes block i."""
+    c = wl.cfg
+    per = c.hkv * c.block * c.head_dim
+    halves = buf.view(2, wl.nb, per)
+    idx = torch.from_numpy(blocks).to(buf.device)
+    return halves.index_select(1, idx).cpu().numpy().reshape(-1)
+
+
+def mini_workload(wl, rows, blocks):
+    """The workload restricted to ``rows`` over a pool holding only ``blocks``
+    (relabelled 0..n-1): other sequences are inactive and have empty tables.
+    The oracle run on it computes exactly the sampled rows of the full one."""
+    import dataclasses
+    remap = np.full(wl.nb, -1, dtype=np.int64)
+    remap[blocks] = np.arange(blocks.size)
+    def relabel(t):
+        out = np.full_like(t, -1)
+        sub = t[rows]
+        out[rows] = np.where(sub >= 0, remap[np.maximum(sub, 0)], -1).astype(t.dtype)
+        return out
+    active = np.zeros_like(wl.active)
+    active[rows] = wl.active[rows]
+    return dataclasses.replace(wl, nb=int(blocks.size), active=active,
+                               bt_full=relabel(wl.bt_full), bt_swa=relabel(wl.bt_swa),
+                               referenced=None)
