@@ -50,8 +50,6 @@ constexpr float kRescaleSlack = 8.0f; // log2 units
 #define PKV_DEPTH 6
 #endif
 constexpr int kDepth = PKV_DEPTH;     // sub-tiles in flight per wave
-constexpr int kChunksPerWorker = 2;   // chunks of the item line per wave, on average
-constexpr int kMinChunk = 8;          // sub-tiles
 constexpr int kTinyItem = 8;          // items this short (sub-tiles) are never split
 // Waves per SIMD the kernel is compiled for (= workgroups per CU, 4 waves
 // each); the stream-K shares assume every worker is resident at once.
@@ -69,7 +67,7 @@ struct AttnArgs {
   uint16_t* out;
   float* partial;
   int32_t* counters;  // [B * Hkv] arrival counters of split items
-  int32_t* queue;     // [2]: next chunk, waves that have left
+  int32_t partial_bytes;
   int64_t nb;
   int32_t B, Hq, Hkv, G;
   int32_t bt_stride, table_width, window;
@@ -94,7 +92,7 @@ __device__ __forceinline__ int seq_subtiles(const AttnArgs& a, int fp, int* lo_o
   return fp / kSub - lo / kSub + 1;
 }
 
-__device__ void block_exclusive_scan(int* s, int n) {
+__device__ __forceinline__ void block_exclusive_scan(int* s, int n) {
   __shared__ int wsum[kWavesPerWG];
   const int tid = threadIdx.x;
   const int per = (n + kThreads - 1) / kThreads;
@@ -186,6 +184,8 @@ struct Stage {
 //    s(t) = (t & ~3) | ((t + (t >> 3)) & 3), so the four tokens 8q+i read
 //    together by the four lane groups fall in different banks.
 constexpr int kSlotBytes = 4096;
+constexpr int kWinRegs = 4;                  // table window: 64 entries per register
+constexpr int kWinEntries = 64 * kWinRegs;
 typedef __attribute__((address_space(3))) uint8_t* lds_ptr_t;
 typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 
@@ -252,8 +252,8 @@ struct Item {
   int nb32;             // num_blocks clamped to int32 (block ids are int32)
   int hkv, h;
   int clo, chi;         // first / last logical block holding keys
-  int tab_base;         // logical block held by lane 0 of `tab`
-  int tab;              // table entries for logical blocks tab_base + lane
+  int tab_base;         // logical block held by lane 0 of tab[0]
+  int tab[kWinRegs];    // table entries for logical blocks tab_base + 64 r + lane
   bool bad;
 
   __device__ Item(const AttnArgs& a, int b, int h_, int lo, int hi)
@@ -263,7 +263,8 @@ struct Item {
     chi = hi / BK;
     trow = a.table + static_cast<int64_t>(b) * a.bt_stride;
     tab_base = -1000000;
-    tab = 0;
+#pragma unroll
+    for (int r = 0; r < kWinRegs; ++r) tab[r] = 0;
   }
 
   // Load the table entries of logical blocks c0 .. c0+63 (one per lane).
@@ -271,14 +272,24 @@ struct Item {
   // K/V loads are in flight.
   __device__ __forceinline__ void load_window(int c0) {
     tab_base = c0;
-    const int cc = c0 + lane_id();
-    tab = (cc <= chi) ? trow[cc] : 0;
+#pragma unroll
+    for (int r = 0; r < kWinRegs; ++r) {
+      const int cc = c0 + 64 * r + lane_id();
+      tab[r] = (cc <= chi) ? trow[cc] : 0;
+    }
   }
 
   // Block id of logical block c (uniform, inside the loaded window).
   // Out-of-range ids are replaced by 0 and flagged.
   __device__ __forceinline__ int block_of(int c) {
-    int blk = __builtin_amdgcn_readlane(tab, c - tab_base);
+    const int i = c - tab_base;
+    const int sel = i >> 6;
+    int blk = __builtin_amdgcn_readlane(tab[0], i & 63);
+#pragma unroll
+    for (int r = 1; r < kWinRegs; ++r) {
+      const int br = __builtin_amdgcn_readlane(tab[r], i & 63);
+      blk = (sel == r) ? br : blk;
+    }
     if (blk < 0 || blk >= nb32) {
       bad = true;
       blk = 0;
@@ -443,6 +454,103 @@ __device__ __forceinline__ void store_bf16x16(uint16_t* dst, const float* v) {
 }
 
 constexpr int kSlotFloats = 8 * kHeadDim + 16;  // o[8][64], m[8], l[8]
+constexpr int kSlotBytesF = kSlotFloats * 4;
+
+// Chunks of the item line [0, total): chunk c covers [c*C, (c+1)*C).  The
+// pieces of one item are in consecutive chunks and use partial slots 2c (the
+// piece continues an item begun in an earlier chunk) or 2c+1 (the piece
+// begins an item that goes on).
+struct Sched {
+  int64_t C;
+  __device__ __forceinline__ int of(int64_t x) const { return static_cast<int>(x / C); }
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(const AttnArgs& a) {
+  return __builtin_amdgcn_make_buffer_rsrc(a.partial, 0, a.partial_bytes, kRsrcWord3);
+}
+constexpr int kCoherent = 16;  // sc1: device-coherent access (write-through / no stale L2 hit)
+
+// Write one piece's partial (o unnormalised, running max m, sum l) to a slot.
+// Lane (m, q) with e == 0 holds o of head g = m, dims 16q .. 16q+15.
+__device__ __forceinline__ void write_partial(const AttnArgs& a, int slot, const float (&o)[16],
+                                              float mx, float lsum, int lane) {
+  const int m = lane & 15, q = lane >> 4;
+  const __amdgpu_buffer_rsrc_t r = partial_rsrc(a);
+  const int base = slot * kSlotBytesF;
+  if (m < 8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4_t w = {__float_as_uint(o[4 * i]), __float_as_uint(o[4 * i + 1]),
+                         __float_as_uint(o[4 * i + 2]), __float_as_uint(o[4 * i + 3])};
+      __builtin_amdgcn_raw_buffer_store_b128(w, r, base + (m * kHeadDim + 16 * q + 4 * i) * 4, 0,
+                                             kCoherent);
+    }
+    if (q == 0) {
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(mx), r, base + (8 * kHeadDim + m) * 4, 0,
+                                            kCoherent);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lsum), r,
+                                            base + (8 * kHeadDim + 8 + m) * 4, 0, kCoherent);
+    }
+  }
+}
+
+// Combine the P pieces of item (b, h) -- chunk cf's tail slot, then the head
+// slots of chunks cf+1 .. cf+P-1 -- and write the output row.  Eight pieces
+// are fetched per round trip; lane (g = lane & 7, part = lane >> 3) owns
+// dims 8*part .. 8*part+7 of head g.  Rounds combine with a running maximum.
+__device__ __forceinline__ void merge_item(const AttnArgs& a, int b, int h, int cf, int P, int lane) {
+  const int g = lane & 7, part = lane >> 3;
+  const __amdgpu_buffer_rsrc_t r = partial_rsrc(a);
+  float mrun = -INFINITY, lrun = 0.f;
+  float acc[8];
+#pragma unroll
+  for (int d = 0; d < 8; ++d) acc[d] = 0.f;
+  for (int k0 = 0; k0 < P; k0 += 8) {
+    float mk[8], lk[8];
+    u32x4_t o0[8], o1[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int k = min(k0 + i, P - 1);
+      const int sl = (k == 0) ? 2 * cf + 1 : 2 * (cf + k);
+      const int base = sl * kSlotBytesF;
+      mk[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, base + (8 * kHeadDim + g) * 4, 0, kCoherent));
+      lk[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, base + (8 * kHeadDim + 8 + g) * 4, 0, kCoherent));
+      o0[i] = __builtin_amdgcn_raw_buffer_load_b128(r, base + (g * kHeadDim + 8 * part) * 4, 0, kCoherent);
+      o1[i] = __builtin_amdgcn_raw_buffer_load_b128(r, base + (g * kHeadDim + 8 * part + 4) * 4, 0, kCoherent);
+    }
+    float mx = mrun;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (k0 + i < P) mx = fmaxf(mx, mk[i]);
+    const float sc = __builtin_amdgcn_exp2f(mrun - mx);
+    lrun *= sc;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) acc[d] *= sc;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (k0 + i < P) {
+        const float w = __builtin_amdgcn_exp2f(mk[i] - mx);
+        lrun += w * lk[i];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          acc[d] += w * __uint_as_float(o0[i][d]);
+          acc[4 + d] += w * __uint_as_float(o1[i][d]);
+        }
+      }
+    }
+    mrun = mx;
+  }
+  if (g < a.G) {
+    const float f = a.v_scale / lrun;
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = static_cast<uint32_t>(f32_to_bf16_bits(acc[2 * i] * f)) |
+             (static_cast<uint32_t>(f32_to_bf16_bits(acc[2 * i + 1] * f)) << 16);
+    *reinterpret_cast<u32x4_t*>(a.out + (static_cast<int64_t>(b) * a.Hq + h * a.G + g) * kHeadDim +
+                                8 * part) = u32x4_t{w[0], w[1], w[2], w[3]};
+  }
+}
 
 // Offset (in the item line) of the first item that starts at or after x;
 // `total` when there is none.  Items are (b, h) in order, sequence b holding
@@ -463,13 +571,13 @@ __device__ __forceinline__ int64_t first_item_start_at_or_after(const int* s_pre
   return static_cast<int64_t>(s_pre[lo_i + 1]) * hkv;  // first item of the next sequence with work
 }
 
-// Process the sub-tiles [cur, wend) of the item line: chunk `wid` of size
-// `chunk`.  Items that lie wholly inside are written out; pieces of items cut
-// by chunk boundaries go through partial slots 2*wid (head) / 2*wid+1 (tail)
-// and are merged by the last piece to arrive.
+// Process the sub-tiles [cur, wend) of the item line, chunk `cid` of the
+// schedule.  Items that lie wholly inside are written out; pieces of items
+// cut by chunk boundaries go through partial slots 2*cid / 2*cid+1 and are
+// merged by the last piece to arrive.
 template <int BK, bool WINDOWED>
-__device__ __forceinline__ void process_chunk(const AttnArgs& a, const int* s_pre, int B, int wid,
-                                              int64_t chunk, int64_t cur, int64_t wend,
+__device__ __forceinline__ void process_chunk(const AttnArgs& a, const int* s_pre, int B, int cid,
+                                              const Sched sc, int64_t cur, int64_t wend,
                                               uint8_t* ring) {
   const int lane = lane_id();
   const int m = lane & 15, q = lane >> 4, e = m >> 3, g = m & 7;
@@ -530,16 +638,16 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const int* s_pr
     const int tlast = t0 + seg - 1;
 
     // Two-stage software pipeline over the segment's sub-tiles, run per
-    // window of 64 table entries.
+    // window of kWinEntries table entries.
     // The first run of a segment is shortened by a per-wave amount so that the
     // waves of a workgroup reach their run boundaries (where the ring drains
     // and refills) at different times and cover each other's bubbles.
-    int span = __builtin_amdgcn_readfirstlane(64 - 16 * ((threadIdx.x >> 6) & 3));
+    int span = __builtin_amdgcn_readfirstlane(kWinEntries - 16 * ((threadIdx.x >> 6) & 3));
     for (int tw = t0; tw <= tlast;) {
       const int cw0 = it.clampc((tw * kSub) / BK);
       it.load_window(cw0);
       const int twl = max(tw, min(tlast, ((cw0 + span) * BK) / kSub - 1));
-      span = 64;
+      span = kWinEntries;
       // Ring of kDepth slots: sub-tile k lives in slot (k - tw) % kDepth.  While
       // sub-tile k is computed from registers, sub-tile k+1 is read from its
       // slot into the other register stage and up to kDepth-1 later sub-tiles
@@ -596,55 +704,18 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const int* s_pr
         store_bf16x16(a.out + (static_cast<int64_t>(b) * a.Hq + h * a.G + g) * kHeadDim + 16 * q, o);
       }
     } else {
-      const int64_t wfirst = item_beg / chunk, wlast = (item_end - 1) / chunk;
-      const int slot = (item_beg >= wbeg) ? 2 * wid + 1 : 2 * wid;
-      float* ps = a.partial + static_cast<int64_t>(slot) * kSlotFloats;
-      if (e == 0) {
-        float* po = ps + g * kHeadDim + 16 * q;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) st_coherent(po + i, o[i]);
-        if (q == 0) {
-          st_coherent(ps + 8 * kHeadDim + g, s.m);
-          st_coherent(ps + 8 * kHeadDim + 8 + g, bad ? NAN : lsum);
-        }
-      }
+      const int cf = sc.of(item_beg), cl = sc.of(item_end - 1);
+      const int slot = (item_beg >= wbeg) ? 2 * cid + 1 : 2 * cid;
+      write_partial(a, slot, o, s.m, bad ? NAN : lsum, lane);
       wait_vm_stores();
       int old = 0;
       int32_t* ctr = a.counters + static_cast<int64_t>(b) * a.Hkv + h;
       if (lane == 0) old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      old = __shfl(old, 0, 64);
-      const int ncontrib = static_cast<int>(wlast - wfirst + 1);
+      old = __builtin_amdgcn_readfirstlane(__shfl(old, 0, 64));
+      const int ncontrib = cl - cf + 1;
       if (old == ncontrib - 1) {
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        // merge every piece of the item: first worker's tail slot, then the
-        // head slots of the following workers
-        float mm = -INFINITY;
-        for (int k = 0; k < ncontrib; ++k) {
-          const int sl = (k == 0) ? static_cast<int>(2 * wfirst + 1) : static_cast<int>(2 * (wfirst + k));
-          mm = fmaxf(mm, ld_coherent(a.partial + static_cast<int64_t>(sl) * kSlotFloats + 8 * kHeadDim + g));
-        }
-        float acc[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-        float ltot = 0.f;
-        for (int k = 0; k < ncontrib; ++k) {
-          const int sl = (k == 0) ? static_cast<int>(2 * wfirst + 1) : static_cast<int>(2 * (wfirst + k));
-          const float* pk = a.partial + static_cast<int64_t>(sl) * kSlotFloats;
-          const float mk = ld_coherent(pk + 8 * kHeadDim + g);
-          const float lk = ld_coherent(pk + 8 * kHeadDim + 8 + g);
-          const float w = __builtin_amdgcn_exp2f(mk - mm);
-          ltot += w * lk;
-          if (e == 0) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[i] += w * ld_coherent(pk + g * kHeadDim + 16 * q + i);
-          }
-        }
-        if (e == 0 && g < a.G) {
-          const float f = a.v_scale / ltot;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[i] *= f;
-          store_bf16x16(a.out + (static_cast<int64_t>(b) * a.Hq + h * a.G + g) * kHeadDim + 16 * q, acc);
-        }
+        merge_item(a, b, h, cf, ncontrib, lane);
         if (lane == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
@@ -695,24 +766,26 @@ __global__ void __launch_bounds__(kThreads, kWGPerCU * kWavesPerWG / 4) decode_a
     for (int i = tid; i < a.Hq * kHeadDim / 8; i += kThreads) row[i] = u32x4_t{f2, f2, f2, f2};
   }
 
-  // Static split of the item line over the waves.  Wave w's share is the
-  // sub-tile range [w*chunk, (w+1)*chunk).  Short items are never cut: when
-  // every item is tiny or at most half a share, wave w takes the whole items
-  // whose first sub-tile falls in its share (no partials, no merge); otherwise
+  // Static split of the item line over the W waves: wave w's share is the
+  // sub-tile range [w*per, (w+1)*per).  Short items are never cut: when every
+  // item is tiny or at most half a share, wave w takes the whole items whose
+  // first sub-tile falls in its share (no partials, no merge); otherwise
   // shares are exact and cut items are merged through the workspace.
   const int64_t total = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(s_pre[B])) * a.Hkv;
   if (total == 0) return;
+  const int W = a.n_workers;
   const int wid = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerWG + (tid >> 6));
-  const int64_t chunk = (total + a.n_workers - 1) / a.n_workers;
-  const int64_t cb = static_cast<int64_t>(wid) * chunk;
+  const int64_t per = (total + W - 1) / W;
+  const int64_t cb = static_cast<int64_t>(wid) * per;
   if (cb >= total) return;
+  const Sched sc{per};
   const int longest_item = __builtin_amdgcn_readfirstlane(s_longest);
-  if (longest_item <= kTinyItem || 2 * static_cast<int64_t>(longest_item) <= chunk) {
+  if (longest_item <= kTinyItem || 2 * static_cast<int64_t>(longest_item) <= per) {
     const int64_t lo_w = first_item_start_at_or_after(s_pre, B, a.Hkv, cb);
-    const int64_t hi_w = first_item_start_at_or_after(s_pre, B, a.Hkv, min(cb + chunk, total));
-    if (lo_w < hi_w) process_chunk<BK, WINDOWED>(a, s_pre, B, wid, chunk, lo_w, hi_w, ring);
+    const int64_t hi_w = first_item_start_at_or_after(s_pre, B, a.Hkv, min(cb + per, total));
+    if (lo_w < hi_w) process_chunk<BK, WINDOWED>(a, s_pre, B, wid, sc, lo_w, hi_w, ring);
   } else {
-    process_chunk<BK, WINDOWED>(a, s_pre, B, wid, chunk, cb, min(cb + chunk, total), ring);
+    process_chunk<BK, WINDOWED>(a, s_pre, B, wid, sc, cb, min(cb + per, total), ring);
   }
   wait_vmcnt<0>();  // no direct-to-LDS load outlives the wave
 }
@@ -740,8 +813,8 @@ int attn_max_subtiles(int block, int table_width, int window) {
   return static_cast<int>((keys + kSub - 1) / kSub + 1);
 }
 
-// Workspace layout: [arrival counters, B*Hkv int32][queue, 2 int32][partial
-// slots, 2 per chunk], each region 256-byte aligned.
+// Workspace layout: [arrival counters, B*Hkv int32][reserved][partial slots,
+// 2 per chunk, one chunk per worker], each region 256-byte aligned.
 static int64_t counters_bytes(int64_t batch, int kv_heads) {
   return (batch * kv_heads * 4 + 255) / 256 * 256;
 }
@@ -749,7 +822,7 @@ constexpr int64_t kQueueBytes = 256;
 
 int64_t attn_workspace_bytes(int64_t batch, int kv_heads, int n_workers) {
   return counters_bytes(batch, kv_heads) + kQueueBytes +
-         static_cast<int64_t>(2) * kChunksPerWorker * n_workers * kSlotFloats * 4;
+         static_cast<int64_t>(2) * n_workers * kSlotBytesF;
 }
 
 hipError_t launch_decode_attn(const AttnLaunch& L, hipStream_t stream) {
@@ -762,7 +835,6 @@ hipError_t launch_decode_attn(const AttnLaunch& L, hipStream_t stream) {
   a.out = L.out;
   const int64_t ctr = counters_bytes(L.B, L.Hkv);
   a.counters = reinterpret_cast<int32_t*>(L.workspace);
-  a.queue = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(L.workspace) + ctr);
   a.partial = reinterpret_cast<float*>(reinterpret_cast<char*>(L.workspace) + ctr + kQueueBytes);
   a.nb = L.nb;
   a.B = L.B;
@@ -775,6 +847,7 @@ hipError_t launch_decode_attn(const AttnLaunch& L, hipStream_t stream) {
   a.score_scale = L.sm_scale * L.k_scale * 1.4426950408889634f;
   a.v_scale = L.v_scale;
   a.n_workers = L.n_workers;
+  a.partial_bytes = static_cast<int32_t>(static_cast<int64_t>(2) * L.n_workers * kSlotBytesF);
   // the workspace holds partial slots for at most this many workers
   if (a.n_workers < kWavesPerWG || a.n_workers > kMaxWorkers || a.n_workers % kWavesPerWG)
     return hipErrorInvalidValue;
