@@ -250,24 +250,33 @@ struct Item {
   const uint8_t* vbase;
   const int32_t* trow;
   int nb32;             // num_blocks clamped to int32 (block ids are int32)
+  int width;            // table entries per row
   int hkv, h;
   int clo, chi;         // first / last logical block holding keys
   int tab_base;         // logical block held by lane 0 of tab[0]
   int tab[kWinRegs];    // table entries for logical blocks tab_base + 64 r + lane
   bool bad;
 
-  __device__ Item(const AttnArgs& a, int b, int h_, int lo, int hi)
+  __device__ Item(const AttnArgs& a, int b, int h_)
       : kbase(a.k), vbase(a.v), hkv(a.Hkv), h(h_), bad(false) {
     nb32 = a.nb > 0x7fffffff ? 0x7fffffff : static_cast<int>(a.nb);
-    clo = lo / BK;
-    chi = hi / BK;
+    width = a.table_width;
+    clo = 0;
+    chi = 0;
     trow = a.table + static_cast<int64_t>(b) * a.bt_stride;
     tab_base = -1000000;
 #pragma unroll
     for (int r = 0; r < kWinRegs; ++r) tab[r] = 0;
   }
 
-  // Load the table entries of logical blocks c0 .. c0+63 (one per lane).
+  // Keys lo .. hi: logical blocks lo/BK .. hi/BK.
+  __device__ __forceinline__ void set_range(int lo, int hi) {
+    clo = lo / BK;
+    chi = hi / BK;
+  }
+
+  // Load the table entries of logical blocks c0 .. c0+kWinEntries-1 (entries
+  // past the row's width read as 0; only blocks clo .. chi are ever used).
   // Done between pipelined runs only, so no table load is ever pending while
   // K/V loads are in flight.
   __device__ __forceinline__ void load_window(int c0) {
@@ -275,7 +284,7 @@ struct Item {
 #pragma unroll
     for (int r = 0; r < kWinRegs; ++r) {
       const int cc = c0 + 64 * r + lane_id();
-      tab[r] = (cc <= chi) ? trow[cc] : 0;
+      tab[r] = (cc < width) ? trow[cc] : 0;
     }
   }
 
@@ -604,19 +613,26 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const int* s_pr
     const int seg = static_cast<int>(min(static_cast<int64_t>(n - j), wend - cur));
     const int64_t item_beg = static_cast<int64_t>(pre_b) * a.Hkv + static_cast<int64_t>(h) * n;
     const int64_t item_end = item_beg + n;
-    const int hi = __builtin_amdgcn_readfirstlane(a.frame_pos[b]);
+    // The item's frame position, its first table window and its queries are
+    // loaded together.  Without a window the keys start at 0, so the first
+    // sub-tile (j) and its table window do not depend on the position.
+    const int fp_raw = a.frame_pos[b];
+    Item<BK, WINDOWED> it(a, b, h);
+    if (!WINDOWED) it.load_window((j * kSub) / BK);
+    u32x4_t q0 = {0u, 0u, 0u, 0u}, q1 = {0u, 0u, 0u, 0u};
+    if (g < a.G) {
+      const uint16_t* qp = a.q + (static_cast<int64_t>(b) * a.Hq + h * a.G + g) * kHeadDim + 16 * q;
+      q0 = *reinterpret_cast<const u32x4_t*>(qp);
+      q1 = *reinterpret_cast<const u32x4_t*>(qp + 8);
+    }
+    const int hi = __builtin_amdgcn_readfirstlane(fp_raw);
     const int lo = WINDOWED ? max(0, hi - a.window + 1) : 0;
+    it.set_range(lo, hi);
+    if (WINDOWED) it.load_window(it.clampc(((lo / kSub + j) * kSub) / BK));
 
     // expanded queries: qx[i][k] holds q[g][16q + 4i + k] in the half of parity e
     uint32_t qx[4][4];
     {
-      u32x4_t q0 = {0u, 0u, 0u, 0u}, q1 = {0u, 0u, 0u, 0u};
-      if (g < a.G) {
-        const uint16_t* qp =
-            a.q + (static_cast<int64_t>(b) * a.Hq + h * a.G + g) * kHeadDim + 16 * q;
-        q0 = *reinterpret_cast<const u32x4_t*>(qp);
-        q1 = *reinterpret_cast<const u32x4_t*>(qp + 8);
-      }
       const uint32_t qw[8] = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -628,7 +644,6 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const int* s_pr
         }
     }
 
-    Item<BK, WINDOWED> it(a, b, h, lo, hi);
     State s;
 #pragma unroll
     for (int t = 0; t < 4; ++t) s.acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -645,7 +660,7 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const int* s_pr
     int span = __builtin_amdgcn_readfirstlane(kWinEntries - 16 * ((threadIdx.x >> 6) & 3));
     for (int tw = t0; tw <= tlast;) {
       const int cw0 = it.clampc((tw * kSub) / BK);
-      it.load_window(cw0);
+      if (cw0 != it.tab_base) it.load_window(cw0);
       const int twl = max(tw, min(tlast, ((cw0 + span) * BK) / kSub - 1));
       span = kWinEntries;
       // Ring of kDepth slots: sub-tile k lives in slot (k - tw) % kDepth.  While
@@ -801,6 +816,7 @@ hipError_t launch(const AttnArgs& a, int n_wg, size_t lds, hipStream_t stream) {
 int attn_workers(int64_t batch, int kv_heads, int max_subtiles) {
   const int64_t total = batch * kv_heads * static_cast<int64_t>(max_subtiles);
   int64_t w = (total + kMinSubtilesPerWorker - 1) / kMinSubtilesPerWorker;
+  if (w < batch * kv_heads) w = batch * kv_heads;  // short items: one wave each
   w = (w + kWavesPerWG - 1) / kWavesPerWG * kWavesPerWG;
   if (w < kWavesPerWG) w = kWavesPerWG;
   if (w > kMaxWorkers) w = kMaxWorkers / kWavesPerWG * kWavesPerWG;
