@@ -177,10 +177,20 @@ typedef struct pkv_step {
 } pkv_step;
 
 /* One layer of the alternating schedule ("Kernel contract"): layer i writes
- * its new K/V into buffer i/2 through upd_swa (i even) or upd_full (i odd),
- * then attends with the trimmed table, window-frame positions and window
- * `step->window` (i even) or the full table, p and no window (i odd).
- * Shapes as in pkv_kv_cache_update / pkv_paged_decode_attn. */
+ * its new K/V into buffer i/2 and attends with the trimmed table,
+ * window-frame positions and window `step->window` (i even) or the full
+ * table, p and no window (i odd).  Shapes as in pkv_kv_cache_update /
+ * pkv_paged_decode_attn.
+ *
+ * Both happen in one launch: the attention quantises each active sequence's
+ * new token (code = E4M3(fp32(x) / fp32(scale))), stores it in the slot the
+ * layer's table gives for the sequence's frame position -- the slot
+ * upd_swa / upd_full name when the control comes from pkv_setup_attn_control,
+ * which is this entry point's precondition -- and attends to it.  Buffer
+ * bytes and outputs are identical to pkv_kv_cache_update followed by
+ * pkv_paged_decode_attn.  No id outside [0, num_blocks) is written.  The
+ * block holding a sequence's new token must not appear in another sequence's
+ * table of the same layer (its old bytes could be read there). */
 int pkv_decode_layer(const pkv_step* step, int32_t layer, const uint16_t* q,
                      const uint16_t* k_new, const uint16_t* v_new, float k_scale,
                      float v_scale, float sm_scale, uint16_t* out, void* workspace,

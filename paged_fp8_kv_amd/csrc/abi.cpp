@@ -173,12 +173,15 @@ int64_t pkv_decode_workspace_bytes(int32_t batch, int32_t q_heads, int32_t kv_he
   return pkv::attn_workspace_bytes(batch, kv_heads, w);
 }
 
-int pkv_paged_decode_attn(int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t head_dim,
-                          int32_t block, int64_t num_blocks, int32_t window, const uint16_t* q,
-                          const uint8_t* k_half, int32_t k_packed, const uint8_t* v_half,
-                          const int32_t* block_table, int32_t bt_stride, int32_t table_width,
-                          const int32_t* frame_pos, float k_scale, float v_scale, float sm_scale,
-                          uint16_t* out, void* workspace, int64_t workspace_bytes, void* stream) {
+// Attention, optionally with the fused write of each sequence's new token
+// (k_new / v_new rows into the writable halves k_w / v_w; see pkv_decode_layer).
+static int attn_impl(int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t head_dim,
+                     int32_t block, int64_t num_blocks, int32_t window, const uint16_t* q,
+                     const uint8_t* k_half, int32_t k_packed, const uint8_t* v_half,
+                     const int32_t* block_table, int32_t bt_stride, int32_t table_width,
+                     const int32_t* frame_pos, float k_scale, float v_scale, float sm_scale,
+                     uint16_t* out, void* workspace, int64_t workspace_bytes, void* stream,
+                     const uint16_t* k_new, const uint16_t* v_new, uint8_t* k_w, uint8_t* v_w) {
   if (batch < 0) return fail(PKV_ERR_ARG, "batch must be >= 0");
   if (batch == 0) return ok();
   if (batch > pkv::kMaxBatch)
@@ -234,7 +237,23 @@ int pkv_paged_decode_attn(int32_t batch, int32_t q_heads, int32_t kv_heads, int3
   L.v_scale = v_scale;
   L.sm_scale = sm_scale;
   L.n_workers = w;
+  L.k_new = k_new;
+  L.v_new = v_new;
+  L.k_w = k_w;
+  L.v_w = v_w;
   return hip_status(pkv::launch_decode_attn(L, static_cast<hipStream_t>(stream)), "attention launch");
+}
+
+int pkv_paged_decode_attn(int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t head_dim,
+                          int32_t block, int64_t num_blocks, int32_t window, const uint16_t* q,
+                          const uint8_t* k_half, int32_t k_packed, const uint8_t* v_half,
+                          const int32_t* block_table, int32_t bt_stride, int32_t table_width,
+                          const int32_t* frame_pos, float k_scale, float v_scale, float sm_scale,
+                          uint16_t* out, void* workspace, int64_t workspace_bytes, void* stream) {
+  return attn_impl(batch, q_heads, kv_heads, head_dim, block, num_blocks, window, q, k_half,
+                   k_packed, v_half, block_table, bt_stride, table_width, frame_pos, k_scale,
+                   v_scale, sm_scale, out, workspace, workspace_bytes, stream, nullptr, nullptr,
+                   nullptr, nullptr);
 }
 
 int pkv_decode_layer(const pkv_step* s, int32_t layer, const uint16_t* q, const uint16_t* k_new,
@@ -263,19 +282,21 @@ int pkv_decode_layer(const pkv_step* s, int32_t layer, const uint16_t* q, const 
   }
   const bool swa = (layer % 2) == 0;
   if (swa && s->window < 1) return fail(PKV_ERR_ARG, "even layers need window >= 1");
-  st = pkv_kv_cache_update(s->batch, s->kv_heads, s->head_dim, s->block, s->num_blocks, k_new,
-                           v_new, kh, s->k_packed, vh, swa ? s->upd_swa : s->upd_full, k_scale,
-                           v_scale, stream);
-  if (st) return st;
+  // One launch: the attention writes each sequence's new token itself (into
+  // the slot its table gives for the frame position, which is the update
+  // index the setup call derived from the same table) and attends to it from
+  // registers.
+  if (!k_new || !v_new) return fail(PKV_ERR_ARG, "null k_new / v_new");
+  if (!aligned(k_new, 2) || !aligned(v_new, 2)) return fail(PKV_ERR_ARG, "k_new / v_new must be 2-byte aligned");
   if (swa)
-    return pkv_paged_decode_attn(s->batch, s->q_heads, s->kv_heads, s->head_dim, s->block,
-                                 s->num_blocks, s->window, q, kh, s->k_packed, vh, s->bt_swa_trim,
-                                 s->trim_width, s->trim_width, s->pos_swa, k_scale, v_scale,
-                                 sm_scale, out, workspace, workspace_bytes, stream);
-  return pkv_paged_decode_attn(s->batch, s->q_heads, s->kv_heads, s->head_dim, s->block,
-                               s->num_blocks, 0, q, kh, s->k_packed, vh, s->bt_full,
-                               s->bt_full_stride, s->bt_full_width, s->pos_full, k_scale, v_scale,
-                               sm_scale, out, workspace, workspace_bytes, stream);
+    return attn_impl(s->batch, s->q_heads, s->kv_heads, s->head_dim, s->block, s->num_blocks,
+                     s->window, q, kh, s->k_packed, vh, s->bt_swa_trim, s->trim_width,
+                     s->trim_width, s->pos_swa, k_scale, v_scale, sm_scale, out, workspace,
+                     workspace_bytes, stream, k_new, v_new, kh, vh);
+  return attn_impl(s->batch, s->q_heads, s->kv_heads, s->head_dim, s->block, s->num_blocks, 0, q,
+                   kh, s->k_packed, vh, s->bt_full, s->bt_full_stride, s->bt_full_width,
+                   s->pos_full, k_scale, v_scale, sm_scale, out, workspace, workspace_bytes, stream,
+                   k_new, v_new, kh, vh);
 }
 
 int pkv_validate_attn_control(int32_t batch, int32_t block, int32_t window, int64_t num_blocks,

@@ -74,6 +74,12 @@ struct AttnArgs {
   float score_scale;  // sm_scale * k_scale * log2(e)
   float v_scale;
   int32_t n_workers;
+  // fused write of the new tokens (k_new null: none)
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint8_t* k_w;
+  uint8_t* v_w;
+  float k_scale;
 };
 
 // frame range [lo, hi] of sequence b; returns the number of sub-tiles
@@ -248,6 +254,8 @@ template <int BK, bool WINDOWED>
 struct Item {
   const uint8_t* kbase;
   const uint8_t* vbase;
+  uint8_t* kw;          // writable halves, for the fused new-token write
+  uint8_t* vw;
   const int32_t* trow;
   int nb32;             // num_blocks clamped to int32 (block ids are int32)
   int width;            // table entries per row
@@ -258,7 +266,7 @@ struct Item {
   bool bad;
 
   __device__ Item(const AttnArgs& a, int b, int h_)
-      : kbase(a.k), vbase(a.v), hkv(a.Hkv), h(h_), bad(false) {
+      : kbase(a.k), vbase(a.v), kw(a.k_w), vw(a.v_w), hkv(a.Hkv), h(h_), bad(false) {
     nb32 = a.nb > 0x7fffffff ? 0x7fffffff : static_cast<int>(a.nb);
     width = a.table_width;
     clo = 0;
@@ -367,6 +375,19 @@ __device__ __forceinline__ void read_slot(const uint8_t* ring, int slot, Stage& 
                                                  (m >> 2) * 16 + (m & 3) * 4);
 }
 
+// Put the new token's codes (lane j: dim j) into a filled slot, at token
+// `tok` (0..31) of the sub-tile, in the slot's own arrangement: K pair row
+// tok/2, byte 2j + tok%2 of the row, rows chunk-swizzled; V row of token tok.
+__device__ __forceinline__ void patch_slot(uint8_t* ring, int slot, int tok, uint32_t kcode,
+                                           uint32_t vcode) {
+  const int j = lane_id();
+  uint8_t* dst = ring + slot * kSlotBytes;
+  const int r = tok >> 1;
+  const int kb = 2 * j + (tok & 1);
+  dst[r * 128 + (((kb >> 4) ^ fk_swz(r)) << 4) + (kb & 15)] = static_cast<uint8_t>(kcode);
+  dst[2048 + v_row_slot(tok) * kHeadDim + j] = static_cast<uint8_t>(vcode);
+}
+
 // One 32-token sub-tile: scores, online-softmax update and PV accumulation.
 // MASKED selects the edge path (keys outside [lo, hi] removed); the stage
 // registers are never written here, so the interior path carries no copies.
@@ -460,6 +481,28 @@ __device__ __forceinline__ void store_bf16x16(uint16_t* dst, const float* v) {
   u32x4_t* d = reinterpret_cast<u32x4_t*>(dst);
   d[0] = u32x4_t{w[0], w[1], w[2], w[3]};
   d[1] = u32x4_t{w[4], w[5], w[6], w[7]};
+}
+
+// Fused cache write of the new token at frame position hi of the item
+// (lane j: dim j): patch the slot holding its sub-tile, and store the codes
+// into the block the table gives for hi (skipped, like the separate update,
+// when that id is outside the pool -- the item is then flagged bad).
+template <int BK, bool WINDOWED>
+__device__ __forceinline__ void write_new_token(Item<BK, WINDOWED>& it, uint8_t* ring, int slot,
+                                                int hi, uint32_t kcode, uint32_t vcode) {
+  patch_slot(ring, slot, hi % kSub, kcode, vcode);
+  const bool was_bad = it.bad;
+  it.bad = false;
+  const int blk = it.block_of(it.clampc(hi / BK));
+  const bool valid = !it.bad;
+  it.bad = was_bad || it.bad;
+  if (valid) {
+    const int j = lane_id();
+    const int tok = hi % BK;
+    const int64_t tile = (static_cast<int64_t>(blk) * it.hkv + it.h) * (BK * kHeadDim);
+    it.kw[tile + ((tok >> 1) * kHeadDim + j) * 2 + (tok & 1)] = static_cast<uint8_t>(kcode);
+    it.vw[tile + tok * kHeadDim + j] = static_cast<uint8_t>(vcode);
+  }
 }
 
 constexpr int kSlotFloats = 8 * kHeadDim + 16;  // o[8][64], m[8], l[8]
@@ -644,6 +687,18 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const int* s_pr
         }
     }
 
+    // The new token (frame position hi) is in sub-tile t_new; with a fused
+    // write, the segment holding it quantises the token's K/V (lane j: dim j),
+    // patches them into that sub-tile's slot before it is read, and stores
+    // them into the cache slot of position hi.
+    const int t_new = (a.k_new != nullptr && hi / kSub >= lo / kSub + j &&
+                       hi / kSub < lo / kSub + j + seg) ? hi / kSub : -1;
+    uint32_t kcode = 0, vcode = 0;
+    if (t_new >= 0) {
+      const int64_t row = (static_cast<int64_t>(b) * a.Hkv + h) * kHeadDim + lane;
+      kcode = f32_to_e4m3_rne_sat(__fdiv_rn(bf16_bits_to_f32(a.k_new[row]), a.k_scale));
+      vcode = f32_to_e4m3_rne_sat(__fdiv_rn(bf16_bits_to_f32(a.v_new[row]), a.v_scale));
+    }
     State s;
 #pragma unroll
     for (int t = 0; t < 4; ++t) s.acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -673,6 +728,7 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const int* s_pr
         if (tw + d <= twl) it.issue(ring, d, tw + d);
       Stage st[2];
       wait_vmcnt_slots(min(twl - tw, kDepth - 1));
+      if (tw == t_new) write_new_token(it, ring, 0, hi, kcode, vcode);
       read_slot(ring, 0, st[0]);
       for (int i = tw; i <= twl; i += kDepth) {
 #pragma unroll
@@ -683,6 +739,7 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const int* s_pr
           // it (t32+2 .. min(twl, t32+kDepth-1)) are outstanding
           if (t32 < twl) {
             wait_vmcnt_slots(min(twl - t32 - 1, kDepth - 2));
+            if (t32 + 1 == t_new) write_new_token(it, ring, (d + 1) % kDepth, hi, kcode, vcode);
             read_slot(ring, (d + 1) % kDepth, st[(d + 1) & 1]);
           }
           if (t32 * kSub >= lo && t32 * kSub + kSub - 1 <= hi)
@@ -862,6 +919,11 @@ hipError_t launch_decode_attn(const AttnLaunch& L, hipStream_t stream) {
   a.window = L.window;
   a.score_scale = L.sm_scale * L.k_scale * 1.4426950408889634f;
   a.v_scale = L.v_scale;
+  a.k_scale = L.k_scale;
+  a.k_new = L.k_new;
+  a.v_new = L.v_new;
+  a.k_w = L.k_w;
+  a.v_w = L.v_w;
   a.n_workers = L.n_workers;
   a.partial_bytes = static_cast<int32_t>(static_cast<int64_t>(2) * L.n_workers * kSlotBytesF);
   // the workspace holds partial slots for at most this many workers

@@ -24,6 +24,14 @@ struct AttnLaunch {
   int32_t bt_stride, table_width, window;
   float k_scale, v_scale, sm_scale;
   int32_t n_workers;
+  // Optional write of each sequence's new token (null k_new: none).  The new
+  // token sits at the sequence's frame position; its K/V rows
+  // (bf16 [B, Hkv, 64]) are quantised with k_scale / v_scale, stored in the
+  // slot the table gives for that position, and attended from registers.
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint8_t* k_w;
+  uint8_t* v_w;
 };
 
 int attn_max_subtiles(int block, int table_width, int window);
