@@ -9,9 +9,9 @@ every context 8192 tokens, random block tables, synthetic N(0,1) data.
 Prints one JSON line.  `value` is the step's algorithmic KV bytes (K + V FP8
 of every attended key of every layer) divided by the measured step time,
 in GB/s; tokens/s is batch / step time.  The step is replayed as a HIP graph
-(inputs resident in HBM); a second, eager phase brackets every full-layer
-attention launch with events on the launch stream to get the dominant
-kernel's average duration for the roofline.  `cpu_baseline` times the CPU
+(inputs resident in HBM); a second, eager phase issues a step's full-layer
+launches back to back between two events on their stream to get the dominant
+kernel's average launch duration for the roofline (window layers likewise).  `cpu_baseline` times the CPU
 oracle on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5]
@@ -178,16 +178,19 @@ def main():
                               ctl["upd_swa"] if swa else ctl["upd_full"], cfg.block, wl.nb,
                               wl.k_scale[i], wl.v_scale[i])
 
+    def layer(i):
+        if step_desc is not None:
+            P.pkv_decode_layer(step_desc, i, q[i], k_new[i], v_new[i], wl.k_scale[i],
+                               wl.v_scale[i], sm, outs[i], ws_swa if i % 2 == 0 else ws_full)
+        else:
+            update(i)
+            attn(i)
+
     def step():
         P.pkv_setup_attn_control(seq_lens, active, bt_full, bt_swa, cfg.block, win,
                                  positions=positions, out=ctl)
         for i in range(cfg.layers):
-            if step_desc is not None:
-                P.pkv_decode_layer(step_desc, i, q[i], k_new[i], v_new[i], wl.k_scale[i],
-                                   wl.v_scale[i], sm, outs[i], ws_swa if i % 2 == 0 else ws_full)
-            else:
-                update(i)
-                attn(i)
+            layer(i)
 
     # eager warm-up; after the first step the cache holds this step's tokens,
     # so every later step recomputes identical outputs
@@ -230,7 +233,10 @@ def main():
     dt = time.perf_counter() - t0
     ms = dt * 1e3 / args.steps
 
-    # ---- dominant kernel: full-layer attention, bracketed by events on its stream
+    # ---- dominant kernel: the full-layer launches of a step, made exactly as the
+    # step makes them but back to back between two events on their stream (the
+    # layers of a step are independent), so the average is the launch duration
+    # plus the gap between consecutive launches; the same for the window layers
     full_layers = [i for i, k in enumerate(cfg.kinds) if k == "full"]
     swa_layers = [i for i, k in enumerate(cfg.kinds) if k == "swa"]
     ev = []
@@ -240,17 +246,19 @@ def main():
     for _ in range(n_ev_steps):
         P.pkv_setup_attn_control(seq_lens, active, bt_full, bt_swa, cfg.block, win,
                                  positions=positions, out=ctl)
-        for i in range(cfg.layers):
-            update(i)
+        for group, sink in ((full_layers, ev), (swa_layers, ev_swa)):
+            if not group:
+                continue
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
             a.record()
-            attn(i)
+            for i in group:
+                layer(i)
             b.record()
-            (ev if cfg.kinds[i] == "full" else ev_swa).append((a, b))
+            sink.append((a, b, len(group)))
     torch.cuda.synchronize()
-    full_us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
-    swa_us = float(np.mean([a.elapsed_time(b) for a, b in ev_swa])) * 1e3 if ev_swa else None
+    full_us = float(np.mean([a.elapsed_time(b) / n for a, b, n in ev])) * 1e3
+    swa_us = float(np.mean([a.elapsed_time(b) / n for a, b, n in ev_swa])) * 1e3 if ev_swa else None
     for a, b in zip(outs, ref):
         assert torch.equal(a, b), "outputs changed between steps"
 

@@ -668,6 +668,14 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const int* s_pr
       q0 = *reinterpret_cast<const u32x4_t*>(qp);
       q1 = *reinterpret_cast<const u32x4_t*>(qp + 8);
     }
+    // the new token's K/V rows (fused write), fetched with the queries; used
+    // only by the segment holding the token
+    uint16_t kn_bits = 0, vn_bits = 0;
+    if (a.k_new != nullptr) {
+      const int64_t row = (static_cast<int64_t>(b) * a.Hkv + h) * kHeadDim + lane;
+      kn_bits = a.k_new[row];
+      vn_bits = a.v_new[row];
+    }
     const int hi = __builtin_amdgcn_readfirstlane(fp_raw);
     const int lo = WINDOWED ? max(0, hi - a.window + 1) : 0;
     it.set_range(lo, hi);
@@ -695,9 +703,8 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const int* s_pr
                        hi / kSub < lo / kSub + j + seg) ? hi / kSub : -1;
     uint32_t kcode = 0, vcode = 0;
     if (t_new >= 0) {
-      const int64_t row = (static_cast<int64_t>(b) * a.Hkv + h) * kHeadDim + lane;
-      kcode = f32_to_e4m3_rne_sat(__fdiv_rn(bf16_bits_to_f32(a.k_new[row]), a.k_scale));
-      vcode = f32_to_e4m3_rne_sat(__fdiv_rn(bf16_bits_to_f32(a.v_new[row]), a.v_scale));
+      kcode = f32_to_e4m3_rne_sat(__fdiv_rn(bf16_bits_to_f32(kn_bits), a.k_scale));
+      vcode = f32_to_e4m3_rne_sat(__fdiv_rn(bf16_bits_to_f32(vn_bits), a.v_scale));
     }
     State s;
 #pragma unroll
