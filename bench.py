@@ -114,6 +114,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--k-layout", choices=["packed", "unpacked"], default="packed",
+                    help="K half arrangement: packed token pairs (default) or token-major rows")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -157,8 +159,9 @@ def main():
     outs = [torch.empty_like(q[i]) for i in range(cfg.layers)]
     sm = 1.0 / float(np.sqrt(cfg.head_dim))
     alternating = all(k == ("swa" if i % 2 == 0 else "full") for i, k in enumerate(cfg.kinds))
+    kp = args.k_layout == "packed"
     step_desc = P.make_step(bufs, ctl, bt_full, cfg.batch, cfg.hq, cfg.hkv, cfg.head_dim,
-                            cfg.block, cfg.window, wl.nb) if alternating else None
+                            cfg.block, cfg.window, wl.nb, k_packed=kp) if alternating else None
 
     def attn(i):
         swa = cfg.kinds[i] == "swa"
@@ -166,17 +169,17 @@ def main():
         if swa:
             P.pkv_paged_decode_attn(q[i], buf, ctl["bt_swa_trim"], ctl["pos_swa"], cfg.block,
                                     wl.nb, cfg.window, wl.k_scale[i], wl.v_scale[i], sm, cfg.hkv,
-                                    out=outs[i], workspace=ws_swa)
+                                    out=outs[i], workspace=ws_swa, k_packed=kp)
         else:
             P.pkv_paged_decode_attn(q[i], buf, bt_full, ctl["pos_full"], cfg.block, wl.nb, 0,
                                     wl.k_scale[i], wl.v_scale[i], sm, cfg.hkv, out=outs[i],
-                                    workspace=ws_full)
+                                    workspace=ws_full, k_packed=kp)
 
     def update(i):
         swa = cfg.kinds[i] == "swa"
         P.pkv_kv_cache_update(bufs[i // 2], k_new[i], v_new[i],
                               ctl["upd_swa"] if swa else ctl["upd_full"], cfg.block, wl.nb,
-                              wl.k_scale[i], wl.v_scale[i])
+                              wl.k_scale[i], wl.v_scale[i], k_packed=kp)
 
     def layer(i):
         if step_desc is not None:
@@ -268,7 +271,8 @@ def main():
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         tr = json.load(open(TRAFFIC_FILE))
-        if tr.get("kernel_sha") == kernel_sha() and tr.get("config") == args.config:
+        if (tr.get("kernel_sha") == kernel_sha() and tr.get("config") == args.config
+                and args.k_layout == "packed"):
             traffic = tr.get("bytes_per_launch")
     value = step_bytes / (ms * 1e-3) / 1e9
     result = {
@@ -287,7 +291,8 @@ def main():
         "config": {"workload": cfg.name, "layers": cfg.layers, "batch": cfg.batch,
                    "q_heads": cfg.hq, "kv_heads": cfg.hkv, "head_dim": cfg.head_dim,
                    "block": cfg.block, "context": "8192" if cfg.ctx[0] == "fixed" else str(cfg.ctx),
-                   "window": cfg.window, "num_blocks": wl.nb, "graph": use_graph},
+                   "window": cfg.window, "num_blocks": wl.nb, "k_layout": args.k_layout,
+                   "graph": use_graph},
         "tokens_per_s": round(cfg.batch / (ms * 1e-3), 1),
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
         "kv_bytes_per_step": step_bytes,

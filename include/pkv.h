@@ -141,6 +141,9 @@ int64_t pkv_decode_workspace_bytes(int32_t batch, int32_t q_heads, int32_t kv_he
  * slot t%block.  out bf16 [batch, q_heads, head_dim] =
  * softmax(sm_scale * q.K^) V^ with K^ = decode(K)*k_scale, V^ = decode(V)*v_scale,
  * accumulated in fp32 and rounded to bf16.
+ * k_packed: 1 = the K half in the packed view [nb, Hkv, block/2, head_dim, 2]
+ * (two tokens interleaved per dimension), 0 = token-major rows
+ * [nb, Hkv, block, head_dim] like V ("KV-cache layout"); same bytes, same speed.
  * workspace: at least pkv_decode_workspace_bytes(...) bytes, 256-byte aligned,
  * zero-filled before first use. */
 int pkv_paged_decode_attn(int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t head_dim,

@@ -205,8 +205,6 @@ static int attn_impl(int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t h
   if (!aligned(block_table, 4) || !aligned(frame_pos, 4))
     return fail(PKV_ERR_ARG, "tables must be 4-byte aligned");
   if (k_packed != 0 && k_packed != 1) return fail(PKV_ERR_ARG, "k_packed must be 0 or 1");
-  if (!k_packed)
-    return fail(PKV_ERR_UNSUPPORTED, "the plain (unpacked) K arrangement is not built yet");
   if (!(k_scale > 0.f) || !(v_scale > 0.f) || !(sm_scale > 0.f) || k_scale == INFINITY ||
       v_scale == INFINITY || sm_scale == INFINITY)
     return fail(PKV_ERR_ARG, "scales must be finite and > 0");
@@ -237,6 +235,7 @@ static int attn_impl(int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t h
   L.v_scale = v_scale;
   L.sm_scale = sm_scale;
   L.n_workers = w;
+  L.k_packed = k_packed;
   L.k_new = k_new;
   L.v_new = v_new;
   L.k_w = k_w;

@@ -250,7 +250,7 @@ __device__ __forceinline__ void wait_vmcnt_slots(int n) {
   }
 }
 
-template <int BK, bool WINDOWED>
+template <int BK, bool WINDOWED, bool KP>
 struct Item {
   const uint8_t* kbase;
   const uint8_t* vbase;
@@ -331,8 +331,10 @@ struct Item {
       const uint32_t so = static_cast<uint32_t>((base % BK) * kHeadDim);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const uint32_t kof = static_cast<uint32_t>((8 * j + (lane >> 3)) * 128 +
-                                                   (((lane & 7) ^ (lane >> 3) ^ j) * 16));
+        const uint32_t kof = KP ? static_cast<uint32_t>((8 * j + (lane >> 3)) * 128 +
+                                                        (((lane & 7) ^ (lane >> 3) ^ j) * 16))
+                                : static_cast<uint32_t>(v_row_token(16 * j + (lane >> 2)) * kHeadDim +
+                                                        (lane & 3) * 16);
         dma16(rk, kof, so, dst + 1024 * j);
       }
 #pragma unroll
@@ -350,9 +352,10 @@ struct Item {
         const int64_t tile = (static_cast<int64_t>(blk) * hkv + h) * (BK * kHeadDim);
         const i32x4_t rk = tile_desc(kbase + tile, BK * kHeadDim);
         const i32x4_t rv = tile_desc(vbase + tile, BK * kHeadDim);
-        const uint32_t kof = static_cast<uint32_t>((lane >> 3) * 128 + (((lane & 7) ^ (lane >> 3) ^ j) * 16));
-        dma16(rk, kof, 0u, dst + 1024 * j);
         const int t = v_row_token(16 * j + (lane >> 2)) - 16 * j;
+        const uint32_t kof = KP ? static_cast<uint32_t>((lane >> 3) * 128 + (((lane & 7) ^ (lane >> 3) ^ j) * 16))
+                                : static_cast<uint32_t>(t * kHeadDim + (lane & 3) * 16);
+        dma16(rk, kof, 0u, dst + 1024 * j);
         const uint32_t vof = static_cast<uint32_t>(t * kHeadDim + (lane & 3) * 16);
         dma16(rv, vof, 0u, dst + 2048 + 1024 * j);
       }
@@ -362,13 +365,26 @@ struct Item {
 
 // Read a filled slot into the MFMA lane layout: K pair row m, bytes
 // [32q, 32q+32); V dwords of tokens 8q..8q+7 at dims 4m..4m+3.
+template <bool KP>
 __device__ __forceinline__ void read_slot(const uint8_t* ring, int slot, Stage& st) {
   const int lane = lane_id();
   const int m = lane & 15, q = lane >> 4;
   const uint8_t* src = ring + slot * kSlotBytes;
-  const int fk = fk_swz(m);
-  st.k0 = *reinterpret_cast<const u32x4_t*>(src + (8 * m + ((2 * q) ^ fk)) * 16);
-  st.k1 = *reinterpret_cast<const u32x4_t*>(src + (8 * m + ((2 * q + 1) ^ fk)) * 16);
+  if constexpr (KP) {
+    const int fk = fk_swz(m);
+    st.k0 = *reinterpret_cast<const u32x4_t*>(src + (8 * m + ((2 * q) ^ fk)) * 16);
+    st.k1 = *reinterpret_cast<const u32x4_t*>(src + (8 * m + ((2 * q + 1) ^ fk)) * 16);
+  } else {
+    // token-major K rows (placed like V): build the packed operand -- pair row
+    // m, bytes [32q, 32q+32) = dims 16q .. 16q+15 of tokens 2m, 2m+1
+    // interleaved -- from 16 bytes of each token's row
+    const u32x4_t t0 = *reinterpret_cast<const u32x4_t*>(src + v_row_slot(2 * m) * kHeadDim + 16 * q);
+    const u32x4_t t1 = *reinterpret_cast<const u32x4_t*>(src + v_row_slot(2 * m + 1) * kHeadDim + 16 * q);
+    st.k0 = u32x4_t{__builtin_amdgcn_perm(t1[0], t0[0], 0x05010400u), __builtin_amdgcn_perm(t1[0], t0[0], 0x07030602u),
+                    __builtin_amdgcn_perm(t1[1], t0[1], 0x05010400u), __builtin_amdgcn_perm(t1[1], t0[1], 0x07030602u)};
+    st.k1 = u32x4_t{__builtin_amdgcn_perm(t1[2], t0[2], 0x05010400u), __builtin_amdgcn_perm(t1[2], t0[2], 0x07030602u),
+                    __builtin_amdgcn_perm(t1[3], t0[3], 0x05010400u), __builtin_amdgcn_perm(t1[3], t0[3], 0x07030602u)};
+  }
 #pragma unroll
   for (int i = 0; i < 8; ++i)
     st.v[i] = *reinterpret_cast<const uint32_t*>(src + 2048 + v_row_slot(8 * q + i) * kHeadDim +
@@ -378,13 +394,18 @@ __device__ __forceinline__ void read_slot(const uint8_t* ring, int slot, Stage& 
 // Put the new token's codes (lane j: dim j) into a filled slot, at token
 // `tok` (0..31) of the sub-tile, in the slot's own arrangement: K pair row
 // tok/2, byte 2j + tok%2 of the row, rows chunk-swizzled; V row of token tok.
+template <bool KP>
 __device__ __forceinline__ void patch_slot(uint8_t* ring, int slot, int tok, uint32_t kcode,
                                            uint32_t vcode) {
   const int j = lane_id();
   uint8_t* dst = ring + slot * kSlotBytes;
-  const int r = tok >> 1;
-  const int kb = 2 * j + (tok & 1);
-  dst[r * 128 + (((kb >> 4) ^ fk_swz(r)) << 4) + (kb & 15)] = static_cast<uint8_t>(kcode);
+  if constexpr (KP) {
+    const int r = tok >> 1;
+    const int kb = 2 * j + (tok & 1);
+    dst[r * 128 + (((kb >> 4) ^ fk_swz(r)) << 4) + (kb & 15)] = static_cast<uint8_t>(kcode);
+  } else {
+    dst[v_row_slot(tok) * kHeadDim + j] = static_cast<uint8_t>(kcode);
+  }
   dst[2048 + v_row_slot(tok) * kHeadDim + j] = static_cast<uint8_t>(vcode);
 }
 
@@ -487,10 +508,10 @@ __device__ __forceinline__ void store_bf16x16(uint16_t* dst, const float* v) {
 // (lane j: dim j): patch the slot holding its sub-tile, and store the codes
 // into the block the table gives for hi (skipped, like the separate update,
 // when that id is outside the pool -- the item is then flagged bad).
-template <int BK, bool WINDOWED>
-__device__ __forceinline__ void write_new_token(Item<BK, WINDOWED>& it, uint8_t* ring, int slot,
+template <int BK, bool WINDOWED, bool KP>
+__device__ __forceinline__ void write_new_token(Item<BK, WINDOWED, KP>& it, uint8_t* ring, int slot,
                                                 int hi, uint32_t kcode, uint32_t vcode) {
-  patch_slot(ring, slot, hi % kSub, kcode, vcode);
+  patch_slot<KP>(ring, slot, hi % kSub, kcode, vcode);
   const bool was_bad = it.bad;
   it.bad = false;
   const int blk = it.block_of(it.clampc(hi / BK));
@@ -500,7 +521,8 @@ __device__ __forceinline__ void write_new_token(Item<BK, WINDOWED>& it, uint8_t*
     const int j = lane_id();
     const int tok = hi % BK;
     const int64_t tile = (static_cast<int64_t>(blk) * it.hkv + it.h) * (BK * kHeadDim);
-    it.kw[tile + ((tok >> 1) * kHeadDim + j) * 2 + (tok & 1)] = static_cast<uint8_t>(kcode);
+    it.kw[KP ? tile + ((tok >> 1) * kHeadDim + j) * 2 + (tok & 1) : tile + tok * kHeadDim + j] =
+        static_cast<uint8_t>(kcode);
     it.vw[tile + tok * kHeadDim + j] = static_cast<uint8_t>(vcode);
   }
 }
@@ -627,7 +649,7 @@ __device__ __forceinline__ int64_t first_item_start_at_or_after(const int* s_pre
 // schedule.  Items that lie wholly inside are written out; pieces of items
 // cut by chunk boundaries go through partial slots 2*cid / 2*cid+1 and are
 // merged by the last piece to arrive.
-template <int BK, bool WINDOWED>
+template <int BK, bool WINDOWED, bool KP>
 __device__ __forceinline__ void process_chunk(const AttnArgs& a, const int* s_pre, int B, int cid,
                                               const Sched sc, int64_t cur, int64_t wend,
                                               uint8_t* ring) {
@@ -660,7 +682,7 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const int* s_pr
     // loaded together.  Without a window the keys start at 0, so the first
     // sub-tile (j) and its table window do not depend on the position.
     const int fp_raw = a.frame_pos[b];
-    Item<BK, WINDOWED> it(a, b, h);
+    Item<BK, WINDOWED, KP> it(a, b, h);
     if (!WINDOWED) it.load_window((j * kSub) / BK);
     u32x4_t q0 = {0u, 0u, 0u, 0u}, q1 = {0u, 0u, 0u, 0u};
     if (g < a.G) {
@@ -736,7 +758,7 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const int* s_pr
       Stage st[2];
       wait_vmcnt_slots(min(twl - tw, kDepth - 1));
       if (tw == t_new) write_new_token(it, ring, 0, hi, kcode, vcode);
-      read_slot(ring, 0, st[0]);
+      read_slot<KP>(ring, 0, st[0]);
       for (int i = tw; i <= twl; i += kDepth) {
 #pragma unroll
         for (int d = 0; d < kDepth; ++d) {
@@ -747,7 +769,7 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const int* s_pr
           if (t32 < twl) {
             wait_vmcnt_slots(min(twl - t32 - 1, kDepth - 2));
             if (t32 + 1 == t_new) write_new_token(it, ring, (d + 1) % kDepth, hi, kcode, vcode);
-            read_slot(ring, (d + 1) % kDepth, st[(d + 1) & 1]);
+            read_slot<KP>(ring, (d + 1) % kDepth, st[(d + 1) & 1]);
           }
           if (t32 * kSub >= lo && t32 * kSub + kSub - 1 <= hi)
             compute_subtile<false>(st[d & 1], t32, lo, hi, a.score_scale, qx, s);
@@ -811,7 +833,7 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const int* s_pr
   }
 }
 
-template <int BK, bool WINDOWED>
+template <int BK, bool WINDOWED, bool KP>
 __global__ void __launch_bounds__(kThreads, kWGPerCU * kWavesPerWG / 4) decode_attn_kernel(AttnArgs a) {
   extern __shared__ int s_pre[];  // [B + 1] prefix of per-sequence sub-tile counts
   __shared__ int s_longest;       // longest item, in sub-tiles
@@ -862,17 +884,23 @@ __global__ void __launch_bounds__(kThreads, kWGPerCU * kWavesPerWG / 4) decode_a
   if (longest_item <= kTinyItem || 2 * static_cast<int64_t>(longest_item) <= per) {
     const int64_t lo_w = first_item_start_at_or_after(s_pre, B, a.Hkv, cb);
     const int64_t hi_w = first_item_start_at_or_after(s_pre, B, a.Hkv, min(cb + per, total));
-    if (lo_w < hi_w) process_chunk<BK, WINDOWED>(a, s_pre, B, wid, sc, lo_w, hi_w, ring);
+    if (lo_w < hi_w) process_chunk<BK, WINDOWED, KP>(a, s_pre, B, wid, sc, lo_w, hi_w, ring);
   } else {
-    process_chunk<BK, WINDOWED>(a, s_pre, B, wid, sc, cb, min(cb + per, total), ring);
+    process_chunk<BK, WINDOWED, KP>(a, s_pre, B, wid, sc, cb, min(cb + per, total), ring);
   }
   wait_vmcnt<0>();  // no direct-to-LDS load outlives the wave
 }
 
-template <int BK, bool WINDOWED>
+template <int BK, bool WINDOWED, bool KP>
 hipError_t launch(const AttnArgs& a, int n_wg, size_t lds, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_attn_kernel<BK, WINDOWED>), dim3(n_wg), dim3(kThreads), lds, stream, a);
+  hipLaunchKernelGGL((decode_attn_kernel<BK, WINDOWED, KP>), dim3(n_wg), dim3(kThreads), lds, stream, a);
   return hipGetLastError();
+}
+
+template <int BK>
+hipError_t launch_bk(const AttnArgs& a, bool win, bool kp, int n_wg, size_t lds, hipStream_t stream) {
+  if (kp) return win ? launch<BK, true, true>(a, n_wg, lds, stream) : launch<BK, false, true>(a, n_wg, lds, stream);
+  return win ? launch<BK, true, false>(a, n_wg, lds, stream) : launch<BK, false, false>(a, n_wg, lds, stream);
 }
 
 }  // namespace
@@ -949,10 +977,10 @@ hipError_t launch_decode_attn(const AttnLaunch& L, hipStream_t stream) {
   const size_t lds = static_cast<size_t>(L.B + 1) * sizeof(int);
   const bool win = L.window > 0;
   switch (L.block) {
-    case 16: return win ? launch<16, true>(a, n_wg, lds, stream) : launch<16, false>(a, n_wg, lds, stream);
-    case 32: return win ? launch<32, true>(a, n_wg, lds, stream) : launch<32, false>(a, n_wg, lds, stream);
-    case 64: return win ? launch<64, true>(a, n_wg, lds, stream) : launch<64, false>(a, n_wg, lds, stream);
-    case 128: return win ? launch<128, true>(a, n_wg, lds, stream) : launch<128, false>(a, n_wg, lds, stream);
+    case 16: return launch_bk<16>(a, win, L.k_packed != 0, n_wg, lds, stream);
+    case 32: return launch_bk<32>(a, win, L.k_packed != 0, n_wg, lds, stream);
+    case 64: return launch_bk<64>(a, win, L.k_packed != 0, n_wg, lds, stream);
+    case 128: return launch_bk<128>(a, win, L.k_packed != 0, n_wg, lds, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -24,6 +24,7 @@ struct AttnLaunch {
   int32_t bt_stride, table_width, window;
   float k_scale, v_scale, sm_scale;
   int32_t n_workers;
+  int32_t k_packed;  // 1: K half in the packed (token-pair interleaved) arrangement
   // Optional write of each sequence's new token (null k_new: none).  The new
   // token sits at the sequence's frame position; its K/V rows
   // (bf16 [B, Hkv, 64]) are quantised with k_scale / v_scale, stored in the

@@ -22,7 +22,7 @@ def alternating(cfg):
     return all(k == ("swa" if i % 2 == 0 else "full") for i, k in enumerate(cfg.kinds))
 
 
-def stale_offsets(wl, per_blk_tokens):
+def stale_offsets(wl, per_blk_tokens, k_packed=True):
     """Byte offsets (K half, V half) of every slot of a referenced block that no
     key of this step reads: slots from the new token onward in the last block
     of each table, and window-table slots outside [p - W + 1, p].  The new
@@ -48,13 +48,13 @@ def stale_offsets(wl, per_blk_tokens):
     toks = np.array(toks, dtype=np.int64)[:, None, None]
     hh = np.arange(H)[None, :, None]
     jj = np.arange(D)[None, None, :]
-    ko = OL.k_offset(blks, hh, toks, jj, H, Bk, D, True).ravel()
+    ko = OL.k_offset(blks, hh, toks, jj, H, Bk, D, k_packed).ravel()
     vo = OL.v_offset(blks, hh, toks, jj, H, Bk, D).ravel()
     return ko, vo
 
 
-def poison_stale(bufs, wl):
-    ko, vo = stale_offsets(wl, None)
+def poison_stale(bufs, wl, k_packed=True):
+    ko, vo = stale_offsets(wl, None, k_packed)
     half = wl.half_bytes
     for buf in bufs:
         k = buf[:half]
@@ -72,7 +72,7 @@ def device_inputs(wl, dev):
                 v_new=wl.v_new.to(dev))
 
 
-def gpu_step(wl, bufs, dev, use_layer_api=True, workspaces=None):
+def gpu_step(wl, bufs, dev, use_layer_api=True, workspaces=None, k_packed=True):
     """Run setup + every layer on the GPU; returns (outputs list, control dict)."""
     c = wl.cfg
     d = device_inputs(wl, dev)
@@ -86,7 +86,7 @@ def gpu_step(wl, bufs, dev, use_layer_api=True, workspaces=None):
     outs = []
     if use_layer_api and alternating(c):
         step = P.make_step(bufs, ctl, d["bt_full"], c.batch, c.hq, c.hkv, c.head_dim, c.block,
-                           c.window, wl.nb)
+                           c.window, wl.nb, k_packed=k_packed)
         for i in range(c.layers):
             out = torch.empty_like(d["q"][i])
             ws = ws_swa if i % 2 == 0 else ws_full
@@ -99,21 +99,22 @@ def gpu_step(wl, bufs, dev, use_layer_api=True, workspaces=None):
             swa = kind == "swa"
             P.pkv_kv_cache_update(buf, d["k_new"][i], d["v_new"][i],
                                   ctl["upd_swa"] if swa else ctl["upd_full"], c.block, wl.nb,
-                                  wl.k_scale[i], wl.v_scale[i])
+                                  wl.k_scale[i], wl.v_scale[i], k_packed=k_packed)
             if swa:
                 out = P.pkv_paged_decode_attn(d["q"][i], buf, ctl["bt_swa_trim"], ctl["pos_swa"],
                                               c.block, wl.nb, c.window, wl.k_scale[i],
-                                              wl.v_scale[i], sm, c.hkv, workspace=ws_swa)
+                                              wl.v_scale[i], sm, c.hkv, workspace=ws_swa,
+                                              k_packed=k_packed)
             else:
                 out = P.pkv_paged_decode_attn(d["q"][i], buf, d["bt_full"], ctl["pos_full"],
                                               c.block, wl.nb, 0, wl.k_scale[i], wl.v_scale[i],
-                                              sm, c.hkv, workspace=ws_full)
+                                              sm, c.hkv, workspace=ws_full, k_packed=k_packed)
             outs.append(out)
     torch.cuda.synchronize()
     return outs, ctl
 
 
-def oracle_step(wl, snaps, layers=None):
+def oracle_step(wl, snaps, layers=None, k_packed=True):
     """snaps: list of host uint8 arrays (whole buffers, pre-step).  Updated in place."""
     c = wl.cfg
     half = wl.half_bytes
@@ -123,7 +124,7 @@ def oracle_step(wl, snaps, layers=None):
     vn = [wl.v_new[i].float().numpy() for i in range(c.layers)]
     return OS.decode_step(bufs, q, kn, vn, wl.seq_lens, wl.active, wl.bt_full, wl.bt_swa,
                           c.block, c.hkv, c.window, wl.k_scale, wl.v_scale,
-                          1.0 / np.sqrt(c.head_dim), True, layers=layers, kinds=list(c.kinds))
+                          1.0 / np.sqrt(c.head_dim), k_packed, layers=layers, kinds=list(c.kinds))
 
 
 def assert_close(got_bf16, ref, what=""):
@@ -173,3 +174,14 @@ def mini_workload(wl, rows, blocks):
     return dataclasses.replace(wl, nb=int(blocks.size), active=active,
                                bt_full=relabel(wl.bt_full), bt_swa=relabel(wl.bt_swa),
                                referenced=None)
+
+
+def packed_to_unpacked(buf, wl):
+    """The same cache with its K half rearranged from the packed view
+    [nb, H, Bk/2, D, 2] to token-major rows [nb, H, Bk, D] (a pure
+    permutation of bytes; the V half is unchanged)."""
+    c = wl.cfg
+    halves = buf.view(2, wl.nb, c.hkv, c.block // 2, c.head_dim, 2)
+    out = buf.clone().view(2, wl.nb, c.hkv, c.block, c.head_dim)
+    out[0] = halves[0].permute(0, 1, 2, 4, 3).reshape(wl.nb, c.hkv, c.block, c.head_dim)
+    return out.view(-1)

@@ -6,7 +6,7 @@ import torch
 import paged_fp8_kv_amd as P
 import workloads as W
 from gpu_harness import (alternating, assert_close, device_inputs, gpu_step, oracle_step,
-                         poison_stale)
+                         packed_to_unpacked, poison_stale)
 from oracle import control as OC
 from oracle import fp8_e4m3 as OF
 from oracle import update as OU
@@ -192,3 +192,40 @@ def test_validate_attn_control(gpu):
         P.pkv_validate_attn_control(d["seq_lens"], d["active"], d["bt_full"],
                                     torch.from_numpy(bad).to(gpu), wl.cfg.block, wl.cfg.window, wl.nb)
     assert e.value.status == P.PKV_ERR_DATA
+
+
+def _small_case_unpacked(name, gpu):
+    wl = W.make_workload(W.CONFIGS[name])
+    host = W.make_buffers(wl, "cpu")
+    poison_stale(host, wl, k_packed=False)
+    snaps = [h.numpy().copy() for h in host]
+    return wl, [h.to(gpu) for h in host], snaps
+
+
+@pytest.mark.parametrize("name", ["cfg1", "cfg2", "cfg5"])
+def test_step_matches_oracle_unpacked_k(name, gpu):
+    """Token-major K rows (the unpacked arrangement): the same step against
+    the oracle reading K through the plain offsets."""
+    print(f"[parity unpacked K] {name}", flush=True)
+    wl, bufs, snaps = _small_case_unpacked(name, gpu)
+    outs, _ = gpu_step(wl, bufs, gpu, k_packed=False)
+    ref, _ = oracle_step(wl, snaps, k_packed=False)
+    for i in range(wl.cfg.layers):
+        assert_close(outs[i], ref[i], f"{name} unpacked layer {i}")
+    for j, b in enumerate(bufs):
+        got = b.cpu().numpy()
+        assert np.array_equal(got, snaps[j]), f"{name} buffer {j}: {int((got != snaps[j]).sum())} bytes differ"
+
+
+@pytest.mark.parametrize("name", ["cfg2", "cfg5"])
+def test_packed_and_unpacked_k_agree_bitwise(name, gpu):
+    """One cache in both K arrangements: identical outputs bit for bit, and
+    the written caches are the same bytes up to the arrangement."""
+    wl, bufs, _ = _small_case(name, gpu)
+    unp = [packed_to_unpacked(b, wl) for b in bufs]
+    a, _ = gpu_step(wl, bufs, gpu)
+    b, _ = gpu_step(wl, unp, gpu, k_packed=False)
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+    for x, y in zip(bufs, unp):
+        assert torch.equal(packed_to_unpacked(x, wl), y)
