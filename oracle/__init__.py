@@ -23,6 +23,7 @@ Modules:
   update     quantize-and-scatter of the new token's K/V
   attention  paged decode attention in float64 (plus a dense brute-force twin)
   step       the alternating SWA/full layer schedule over shared buffers
+  budget     the KV-cache byte and block budget of a device (host policy)
 
 Parity status: every function is pinned by a ``-m "not gpu"`` test (see the
 test modules named ``tests/test_oracle_*.py``); none is "parity unpinned".
