@@ -65,6 +65,27 @@ int pkv_abi_version(void);
 /* Text of the last non-OK status returned on this thread ("" if none). */
 const char* pkv_last_error(void);
 
+/* Host only.  Bytes the KV cache may take on a device ("determine_available_
+ * memory design", "Heuristic formula", "Minimum KV guard" and the shared budget
+ * logic of "How this is implemented"):
+ *   total_budget = int(total_hbm_bytes * gmu)
+ *   available    = max(min(max(total_budget - bytes_used, 0),
+ *                          int(total_budget * cap_fraction)), 0)
+ * with int() truncating toward zero and doubles as in Python (the page's
+ * defaults: cap_fraction 0.30, min_kv_gib 1.0).  *available_bytes (host) is
+ * written in every non-ARG case; a budget below min_kv_gib GiB returns
+ * PKV_ERR_DATA.  Byte counts must lie in [0, 2^52], gmu and cap_fraction in
+ * [0, 1]. */
+int pkv_kv_budget(int64_t total_hbm_bytes, int64_t bytes_used, double gmu,
+                  double cap_fraction, double min_kv_gib, int64_t* available_bytes);
+
+/* Host only.  Blocks per buffer a budget buys ("GPT-OSS-120B giga-kernel
+ * decode", "KV budget (no cap)"): one block id costs both halves of each of
+ * n_buffers shared buffers, 2 * kv_heads * block * head_dim bytes apiece;
+ * rounded down and capped at INT32_MAX (block ids are int32). */
+int pkv_kv_num_blocks(int64_t available_bytes, int32_t n_buffers, int32_t kv_heads,
+                      int32_t block, int32_t head_dim, int64_t* num_blocks);
+
 /* Host only.  Bytes of one half (K or V) and of a whole shared buffer
  * [2, num_blocks, kv_heads, block, head_dim] (section "KV-cache layout"); the
  * packed K view covers the same bytes.  Outputs are host pointers. */

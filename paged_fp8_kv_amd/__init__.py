@@ -49,6 +49,9 @@ _SIGS = {
     "pkv_last_error": ([], ctypes.c_char_p),
     "pkv_kv_buffer_bytes": ([_i64, _i32, _i32, _i32, ctypes.POINTER(_i64), ctypes.POINTER(_i64)], _i32),
     "pkv_trimmed_width": ([_i32, _i32], _i32),
+    "pkv_kv_budget": ([_i64, _i64, ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                       ctypes.POINTER(_i64)], _i32),
+    "pkv_kv_num_blocks": ([_i64, _i32, _i32, _i32, _i32, ctypes.POINTER(_i64)], _i32),
     "pkv_setup_attn_control": ([_i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
                                 _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp], _i32),
     "pkv_kv_cache_update": ([_i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _i32, _vp, _vp,
@@ -117,6 +120,21 @@ def pkv_kv_buffer_bytes(num_blocks, kv_heads, block, head_dim):
     _check(lib().pkv_kv_buffer_bytes(num_blocks, kv_heads, block, head_dim, ctypes.byref(h),
                                      ctypes.byref(t)))
     return h.value, t.value
+
+
+def pkv_kv_budget(total_hbm_bytes, bytes_used, gmu, cap_fraction=0.30, min_kv_gib=1.0):
+    """Bytes the KV cache may take; raises PkvError (PKV_ERR_DATA) below the minimum."""
+    out = _i64()
+    _check(lib().pkv_kv_budget(total_hbm_bytes, bytes_used, gmu, cap_fraction, min_kv_gib,
+                               ctypes.byref(out)))
+    return out.value
+
+
+def pkv_kv_num_blocks(available_bytes, n_buffers, kv_heads, block, head_dim):
+    out = _i64()
+    _check(lib().pkv_kv_num_blocks(available_bytes, n_buffers, kv_heads, block, head_dim,
+                                   ctypes.byref(out)))
+    return out.value
 
 
 def pkv_trimmed_width(window, block):

@@ -77,6 +77,37 @@ int pkv_kv_buffer_bytes(int64_t num_blocks, int32_t kv_heads, int32_t block, int
   return ok();
 }
 
+int pkv_kv_budget(int64_t total_hbm_bytes, int64_t bytes_used, double gmu, double cap_fraction,
+                  double min_kv_gib, int64_t* available_bytes) {
+  if (!available_bytes) return fail(PKV_ERR_ARG, "null output pointer");
+  if (total_hbm_bytes < 0 || bytes_used < 0 || total_hbm_bytes > (int64_t{1} << 52))
+    return fail(PKV_ERR_ARG, "byte counts must be in [0, 2^52]");
+  if (!(gmu >= 0.0 && gmu <= 1.0) || !(cap_fraction >= 0.0 && cap_fraction <= 1.0) ||
+      !(min_kv_gib >= 0.0 && min_kv_gib < 1e9))
+    return fail(PKV_ERR_ARG, "gmu and cap_fraction must be in [0, 1], min_kv_gib >= 0");
+  // int(x) of a double truncates toward zero; byte counts below 2^53 convert exactly
+  const int64_t total_budget = static_cast<int64_t>(static_cast<double>(total_hbm_bytes) * gmu);
+  const int64_t user_budget = std::max<int64_t>(total_budget - bytes_used, 0);
+  const int64_t cap = static_cast<int64_t>(static_cast<double>(total_budget) * cap_fraction);
+  const int64_t available = std::max<int64_t>(std::min(user_budget, cap), 0);
+  *available_bytes = available;
+  if (static_cast<double>(available) < min_kv_gib * 1073741824.0)
+    return fail(PKV_ERR_DATA, "KV budget of %lld bytes is below the minimum of %g GiB",
+                static_cast<long long>(available), min_kv_gib);
+  return ok();
+}
+
+int pkv_kv_num_blocks(int64_t available_bytes, int32_t n_buffers, int32_t kv_heads, int32_t block,
+                      int32_t head_dim, int64_t* num_blocks) {
+  if (!num_blocks) return fail(PKV_ERR_ARG, "null output pointer");
+  if (available_bytes < 0 || n_buffers < 1 || kv_heads < 1 || block < 1 || head_dim < 1)
+    return fail(PKV_ERR_ARG, "sizes must be positive");
+  const int64_t per = int64_t{2} * n_buffers * kv_heads * block * head_dim;
+  const int64_t n = available_bytes / per;
+  *num_blocks = std::min<int64_t>(n, INT32_MAX);  // block ids are int32
+  return ok();
+}
+
 int pkv_trimmed_width(int32_t window, int32_t block) {
   if (window < 1 || block < 1) return fail(PKV_ERR_ARG, "window and block must be >= 1");
   g_err.clear();
