@@ -67,3 +67,36 @@ def attention_control(seq_lens, active, bt_full, bt_swa, block: int, window: int
             pos_abs[b] = int(positions[b])
     return dict(pos_full=pos_full, pos_swa=pos_swa, bt_swa_trim=trim,
                 upd_full=upd_full, upd_swa=upd_swa, pos_abs=pos_abs)
+
+
+def csr_to_tables(kv_indptr, full_indices, swa_indices, last_page_len, block: int, width: int):
+    """Padded per-sequence inputs from compressed page lists.
+
+    "MPK Internals: Compilation-to-Runtime Pipeline", "Phase 4: Runtime
+    Initialization", names the per-step page meta-tensors (`qo_indptr`,
+    `paged_kv_indptr`, `paged_kv_indices`, `paged_kv_last_page_len`) without
+    defining them.  Reading: sequence b's pages are
+    ``full_indices[kv_indptr[b]:kv_indptr[b+1]]`` in logical order; its token
+    count is ``(pages - 1) * block + last_page_len[b]`` (0 pages: no tokens);
+    the sliding-window page list shares ``kv_indptr`` and holds -1 where the
+    window's blocks were freed; a decode step has one query per sequence, so
+    ``qo_indptr`` is the identity and is not needed.
+
+    Returns (seq_lens int32 [B], bt_full int32 [B, width], bt_swa int32
+    [B, width]), -1 beyond each sequence's pages (pages past `width` dropped).
+    """
+    kv_indptr = np.asarray(kv_indptr, dtype=np.int64)
+    B = kv_indptr.size - 1
+    seq_lens = np.zeros(B, dtype=np.int32)
+    bt_full = np.full((B, width), -1, dtype=np.int32)
+    bt_swa = np.full((B, width), -1, dtype=np.int32)
+    for b in range(B):
+        lo, hi = int(kv_indptr[b]), int(kv_indptr[b + 1])
+        n = hi - lo
+        if n > 0:
+            seq_lens[b] = (n - 1) * block + int(last_page_len[b])
+        for c in range(min(n, width)):
+            bt_full[b, c] = full_indices[lo + c]
+            if swa_indices is not None:
+                bt_swa[b, c] = swa_indices[lo + c]
+    return seq_lens, bt_full, bt_swa

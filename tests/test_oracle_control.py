@@ -71,3 +71,51 @@ def test_inactive_and_missing_blocks():
 
 def test_trimmed_width_values():
     assert [C.trimmed_width(W, b) for b in (16, 32, 128)] == [9, 5, 2]
+
+
+def _to_csr(seq_lens, bt_full, bt_swa, block):
+    """Compress padded tables by hand (plain loops, independent of the oracle)."""
+    indptr, full, swa, last = [0], [], [], []
+    for b in range(len(seq_lens)):
+        n = -(-int(seq_lens[b]) // block)
+        for c in range(n):
+            full.append(int(bt_full[b, c])); swa.append(int(bt_swa[b, c]))
+        indptr.append(indptr[-1] + n)
+        last.append(int(seq_lens[b]) - (n - 1) * block if n else 0)
+    return np.array(indptr), np.array(full), np.array(swa), np.array(last)
+
+
+@pytest.mark.parametrize("block", [16, 32, 128])
+def test_csr_round_trip_and_lengths(block):
+    """Padded tables -> compressed page lists -> padded tables is the identity
+    on every referenced column, and lengths follow (pages-1)*block + last."""
+    rng = np.random.default_rng(block)
+    B, width = 40, 70
+    L = rng.integers(0, width * block + 1, size=B).astype(np.int32)
+    L[:3] = [0, 1, width * block]
+    bt_full = np.full((B, width), -1, np.int32)
+    bt_swa = np.full((B, width), -1, np.int32)
+    for b in range(B):
+        n = -(-int(L[b]) // block)
+        bt_full[b, :n] = rng.integers(0, 10**6, n)
+        keep = max(0, n - 5)
+        bt_swa[b, keep:n] = rng.integers(0, 10**6, n - keep)
+    ip, fi, si, lp = _to_csr(L, bt_full, bt_swa, block)
+    sl, f2, s2 = C.csr_to_tables(ip, fi, si, lp, block, width)
+    assert np.array_equal(sl, L)
+    assert np.array_equal(f2, bt_full) and np.array_equal(s2, bt_swa)
+    # the control built from either form is the same
+    act = (L > 0).astype(np.uint8)
+    a = C.attention_control(L, act, bt_full, bt_swa, block, 128)
+    b_ = C.attention_control(sl, act, f2, s2, block, 128)
+    for k in a:
+        assert np.array_equal(a[k], b_[k]), k
+
+
+def test_csr_hand_example():
+    """Two sequences, block 4: 3 pages with 2 tokens in the last (10 tokens),
+    and 1 page with 4 tokens; the window list frees the first page."""
+    sl, f, s = C.csr_to_tables([0, 3, 4], [7, 2, 9, 5], [-1, 11, 12, 13], [2, 4], 4, 5)
+    assert sl.tolist() == [10, 4]
+    assert f.tolist() == [[7, 2, 9, -1, -1], [5, -1, -1, -1, -1]]
+    assert s.tolist() == [[-1, 11, 12, -1, -1], [13, -1, -1, -1, -1]]
