@@ -114,6 +114,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--tables", choices=["padded", "csr"], default="padded",
+                    help="block tables as padded rows (default) or compressed page lists")
     ap.add_argument("--k-layout", choices=["packed", "unpacked"], default="packed",
                     help="K half arrangement: packed token pairs (default) or token-major rows")
     args = ap.parse_args()
@@ -149,8 +151,31 @@ def main():
     q, k_new, v_new = wl.q.to(dev), wl.k_new.to(dev), wl.v_new.to(dev)
     has_swa = "swa" in cfg.kinds
     win = cfg.window if has_swa else 0
-    ctl = P.pkv_setup_attn_control(seq_lens, active, bt_full, bt_swa, cfg.block, win,
-                                   positions=positions)
+    if args.tables == "csr":
+        # the same tables as compressed page lists; the setup writes the padded
+        # full table the layers read
+        Bk = cfg.block
+        n_pages = -(-wl.seq_lens.astype(np.int64) // Bk)
+        indptr = np.concatenate([[0], np.cumsum(n_pages)]).astype(np.int32)
+        full_idx = np.concatenate([wl.bt_full[b, :n_pages[b]] for b in range(cfg.batch)]).astype(np.int32)
+        swa_idx = np.concatenate([wl.bt_swa[b, :n_pages[b]] for b in range(cfg.batch)]).astype(np.int32)
+        last = (wl.seq_lens - (n_pages - 1) * Bk).astype(np.int32)
+        csr = (to(indptr), to(full_idx), to(swa_idx), to(last))
+        ctl = P.pkv_setup_attn_control_csr(*csr, active, cfg.block, win, wl.bt_full.shape[1],
+                                           positions=positions)
+        bt_full = ctl["bt_full"]
+    else:
+        csr = None
+        ctl = P.pkv_setup_attn_control(seq_lens, active, bt_full, bt_swa, cfg.block, win,
+                                       positions=positions)
+
+    def setup():
+        if csr is not None:
+            P.pkv_setup_attn_control_csr(*csr, active, cfg.block, win, wl.bt_full.shape[1],
+                                         positions=positions, out=ctl)
+        else:
+            P.pkv_setup_attn_control(seq_lens, active, bt_full, bt_swa, cfg.block, win,
+                                     positions=positions, out=ctl)
     tw = ctl["bt_swa_trim"].shape[1]
     ws_full = P.new_workspace(cfg.batch, cfg.hq, cfg.hkv, cfg.head_dim, cfg.block,
                               wl.bt_full.shape[1], 0, dev)
@@ -190,8 +215,7 @@ def main():
             attn(i)
 
     def step():
-        P.pkv_setup_attn_control(seq_lens, active, bt_full, bt_swa, cfg.block, win,
-                                 positions=positions, out=ctl)
+        setup()
         for i in range(cfg.layers):
             layer(i)
 
@@ -247,8 +271,7 @@ def main():
     n_ev_steps = max(1, min(args.steps, 5))
     torch.cuda.synchronize()
     for _ in range(n_ev_steps):
-        P.pkv_setup_attn_control(seq_lens, active, bt_full, bt_swa, cfg.block, win,
-                                 positions=positions, out=ctl)
+        setup()
         for group, sink in ((full_layers, ev), (swa_layers, ev_swa)):
             if not group:
                 continue
@@ -272,7 +295,7 @@ def main():
     if os.path.exists(TRAFFIC_FILE):
         tr = json.load(open(TRAFFIC_FILE))
         if (tr.get("kernel_sha") == kernel_sha() and tr.get("config") == args.config
-                and args.k_layout == "packed"):
+                and args.k_layout == "packed" and args.tables == "padded"):
             traffic = tr.get("bytes_per_launch")
     value = step_bytes / (ms * 1e-3) / 1e9
     result = {
@@ -291,7 +314,7 @@ def main():
         "config": {"workload": cfg.name, "layers": cfg.layers, "batch": cfg.batch,
                    "q_heads": cfg.hq, "kv_heads": cfg.hkv, "head_dim": cfg.head_dim,
                    "block": cfg.block, "context": "8192" if cfg.ctx[0] == "fixed" else str(cfg.ctx),
-                   "window": cfg.window, "num_blocks": wl.nb, "k_layout": args.k_layout,
+                   "window": cfg.window, "num_blocks": wl.nb, "k_layout": args.k_layout, "tables": args.tables,
                    "graph": use_graph},
         "tokens_per_s": round(cfg.batch / (ms * 1e-3), 1),
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),

@@ -124,6 +124,28 @@ int pkv_setup_attn_control(int32_t batch, int32_t block, int32_t window,
                            int64_t* upd_full, int64_t* upd_swa, int64_t* pos_abs,
                            void* stream);
 
+/* The same control from compressed page lists instead of padded tables
+ * ("MPK Internals: Compilation-to-Runtime Pipeline", "Phase 4": the
+ * paged_kv_indptr / paged_kv_indices / paged_kv_last_page_len meta-tensors).
+ * Sequence b's pages are full_indices[kv_indptr[b] .. kv_indptr[b+1]) in
+ * logical order; it holds (pages-1)*block + last_page_len[b] tokens (0 pages:
+ * none); swa_indices shares kv_indptr and holds -1 where the window's blocks
+ * were freed (needed when window > 0).  A decode step has one query per
+ * sequence, so no query index array is taken.  Outputs, besides those of
+ * pkv_setup_attn_control: seq_lens int32 [batch] and the padded full table
+ * bt_full int32 [batch, bt_stride] (bt_width columns written, -1 past a
+ * sequence's pages; pages past bt_width are dropped) for
+ * pkv_paged_decode_attn / pkv_step.  All arrays are device arrays; kv_indptr
+ * has batch+1 entries and must be non-decreasing (not checked here). */
+int pkv_setup_attn_control_csr(int32_t batch, int32_t block, int32_t window,
+                               const int32_t* kv_indptr, const int32_t* full_indices,
+                               const int32_t* swa_indices, const int32_t* last_page_len,
+                               const uint8_t* active, const int64_t* positions, int32_t* bt_full,
+                               int32_t bt_stride, int32_t bt_width, int32_t* seq_lens,
+                               int32_t* pos_full, int32_t* pos_swa, int32_t* bt_swa_trim,
+                               int32_t trim_width, int64_t* upd_full, int64_t* upd_swa,
+                               int64_t* pos_abs, void* stream);
+
 /* Quantise and scatter the new token's K and V into one shared buffer
  * ("Kernel contract": the write through an update index; "KV-cache layout":
  * packed K, plain V).

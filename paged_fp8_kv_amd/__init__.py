@@ -54,6 +54,8 @@ _SIGS = {
     "pkv_kv_num_blocks": ([_i64, _i32, _i32, _i32, _i32, ctypes.POINTER(_i64)], _i32),
     "pkv_setup_attn_control": ([_i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
                                 _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp], _i32),
+    "pkv_setup_attn_control_csr": ([_i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
+                                    _i32, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp], _i32),
     "pkv_kv_cache_update": ([_i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _i32, _vp, _vp,
                              _f32, _f32, _vp], _i32),
     "pkv_decode_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32, _i32, _i32], _i64),
@@ -179,6 +181,42 @@ def _halves(buf, num_blocks, kv_heads, block, head_dim):
     if buf.device.type != "cuda":
         raise ValueError("KV buffer must be a device tensor")
     return buf.data_ptr(), buf.data_ptr() + half
+
+
+def pkv_setup_attn_control_csr(kv_indptr, full_indices, swa_indices, last_page_len, active,
+                               block, window, bt_width, positions=None, out=None, stream=None):
+    """Control from compressed page lists.  Returns the dict of
+    pkv_setup_attn_control plus seq_lens and the padded full table bt_full
+    (written into `out` when given, e.g. for graph capture)."""
+    B = kv_indptr.shape[0] - 1
+    tw = pkv_trimmed_width(window, block) if window > 0 else 0
+    dev = kv_indptr.device
+    if out is None:
+        out = dict(
+            bt_full=torch.empty(max(B, 1), bt_width, dtype=torch.int32, device=dev)[:B],
+            seq_lens=torch.empty(B, dtype=torch.int32, device=dev),
+            pos_full=torch.empty(B, dtype=torch.int32, device=dev),
+            pos_swa=torch.empty(B, dtype=torch.int32, device=dev),
+            bt_swa_trim=torch.empty(B, max(tw, 1), dtype=torch.int32, device=dev),
+            upd_full=torch.empty(B, dtype=torch.int64, device=dev),
+            upd_swa=torch.empty(B, dtype=torch.int64, device=dev),
+            pos_abs=torch.empty(B, dtype=torch.int64, device=dev),
+        )
+    _check(lib().pkv_setup_attn_control_csr(
+        B, block, window, _dev_ptr(kv_indptr, torch.int32, "kv_indptr"),
+        _dev_ptr(full_indices, torch.int32, "full_indices"),
+        _dev_ptr(swa_indices, torch.int32, "swa_indices") if window > 0 else None,
+        _dev_ptr(last_page_len, torch.int32, "last_page_len"),
+        _dev_ptr(active, torch.uint8, "active"), _dev_ptr(positions, torch.int64, "positions"),
+        _dev_ptr(out["bt_full"], torch.int32, "bt_full"), bt_width, bt_width,
+        _dev_ptr(out["seq_lens"], torch.int32, "seq_lens"),
+        _dev_ptr(out["pos_full"], torch.int32, "pos_full"),
+        _dev_ptr(out["pos_swa"], torch.int32, "pos_swa"),
+        _dev_ptr(out["bt_swa_trim"], torch.int32, "bt_swa_trim"), tw,
+        _dev_ptr(out["upd_full"], torch.int64, "upd_full"),
+        _dev_ptr(out["upd_swa"], torch.int64, "upd_swa"),
+        _dev_ptr(out["pos_abs"], torch.int64, "pos_abs"), _stream(stream)))
+    return out
 
 
 def pkv_kv_cache_update(buf, k_new, v_new, slot_idx, block, num_blocks, k_scale, v_scale,

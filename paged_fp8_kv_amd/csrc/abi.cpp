@@ -159,6 +159,56 @@ int pkv_setup_attn_control(int32_t batch, int32_t block, int32_t window, const i
   return hip_status(pkv::launch_setup(L, static_cast<hipStream_t>(stream)), "setup launch");
 }
 
+int pkv_setup_attn_control_csr(int32_t batch, int32_t block, int32_t window,
+                               const int32_t* kv_indptr, const int32_t* full_indices,
+                               const int32_t* swa_indices, const int32_t* last_page_len,
+                               const uint8_t* active, const int64_t* positions, int32_t* bt_full,
+                               int32_t bt_stride, int32_t bt_width, int32_t* seq_lens,
+                               int32_t* pos_full, int32_t* pos_swa, int32_t* bt_swa_trim,
+                               int32_t trim_width, int64_t* upd_full, int64_t* upd_swa,
+                               int64_t* pos_abs, void* stream) {
+  if (batch < 0) return fail(PKV_ERR_ARG, "batch must be >= 0");
+  if (batch == 0) return ok();
+  if (batch > INT32_MAX / 2) return fail(PKV_ERR_ARG, "batch too large");
+  if (block < 1 || block % 2) return fail(PKV_ERR_ARG, "block must be a positive even number");
+  if (window < 0) return fail(PKV_ERR_ARG, "window must be >= 0");
+  if (bt_width < 1 || bt_stride < bt_width) return fail(PKV_ERR_ARG, "need 1 <= bt_width <= bt_stride");
+  if (!kv_indptr || !full_indices || !last_page_len || !active || !bt_full || !seq_lens ||
+      !pos_full || !upd_full)
+    return fail(PKV_ERR_ARG, "null device pointer");
+  if (window > 0) {
+    if (!swa_indices || !pos_swa || !bt_swa_trim || !upd_swa)
+      return fail(PKV_ERR_ARG, "window > 0 needs swa_indices, pos_swa, bt_swa_trim and upd_swa");
+    const int need = (window - 1 + block - 1) / block + 1;
+    if (trim_width != need)
+      return fail(PKV_ERR_ARG, "trim_width must be %d for window %d, block %d (got %d)", need,
+                  window, block, trim_width);
+  }
+  pkv::SetupLaunch L{};
+  L.B = batch;
+  L.block = block;
+  L.window = window;
+  L.active = active;
+  L.positions = positions;
+  L.bt_full_stride = bt_stride;
+  L.bt_width = bt_width;
+  L.pos_full = pos_full;
+  L.pos_swa = pos_swa;
+  L.trim = window > 0 ? bt_swa_trim : nullptr;
+  L.trim_width = window > 0 ? trim_width : 0;
+  L.upd_full = upd_full;
+  L.upd_swa = upd_swa;
+  L.pos_abs = pos_abs;
+  pkv::CsrInput C{};
+  C.kv_indptr = kv_indptr;
+  C.full_indices = full_indices;
+  C.swa_indices = window > 0 ? swa_indices : nullptr;
+  C.last_page_len = last_page_len;
+  C.bt_full_out = bt_full;
+  C.seq_lens_out = seq_lens;
+  return hip_status(pkv::launch_setup_csr(L, C, static_cast<hipStream_t>(stream)), "setup launch");
+}
+
 int pkv_kv_cache_update(int32_t batch, int32_t kv_heads, int32_t head_dim, int32_t block,
                         int64_t num_blocks, const uint16_t* k_new, const uint16_t* v_new,
                         uint8_t* k_half, int32_t k_packed, uint8_t* v_half,

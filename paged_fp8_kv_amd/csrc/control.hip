@@ -13,11 +13,11 @@ namespace pkv {
 
 namespace {
 
-__global__ void __launch_bounds__(256) setup_kernel(SetupLaunch a) {
-  const int b = blockIdx.x * 256 + threadIdx.x;
-  if (b >= a.B) return;
+// The control of sequence b from its token count and an accessor for its
+// table rows: full(c) / swa(c) give the block id of logical block c, or -1.
+template <class Full, class Swa>
+__device__ __forceinline__ void setup_one(const SetupLaunch& a, int b, int len, Full full, Swa swa) {
   const int BK = a.block;
-  const int len = a.seq_lens[b];
   const bool act = a.active[b] != 0 && len > 0;
   int32_t* trow = a.trim ? a.trim + static_cast<int64_t>(b) * a.trim_width : nullptr;
   if (!act) {
@@ -36,24 +36,47 @@ __global__ void __launch_bounds__(256) setup_kernel(SetupLaunch a) {
   const bool in_table = cp < a.bt_width;
   a.pos_full[b] = p;
   {
-    const int blk = in_table ? a.bt_full[static_cast<int64_t>(b) * a.bt_full_stride + cp] : -1;
+    const int blk = in_table ? full(cp) : -1;
     a.upd_full[b] = blk >= 0 ? static_cast<int64_t>(blk) * BK + p % BK : -1;
   }
   if (a.window > 0) {
     const int first = max(0, p - a.window + 1) / BK;
-    const int32_t* srow = a.bt_swa + static_cast<int64_t>(b) * a.bt_swa_stride;
     for (int i = 0; i < a.trim_width; ++i) {
       const int c = first + i;
-      trow[i] = (c <= cp && c < a.bt_width) ? srow[c] : -1;
+      trow[i] = (c <= cp && c < a.bt_width) ? swa(c) : -1;
     }
     a.pos_swa[b] = p - first * BK;
-    const int blk = in_table ? srow[cp] : -1;
+    const int blk = in_table ? swa(cp) : -1;
     a.upd_swa[b] = blk >= 0 ? static_cast<int64_t>(blk) * BK + p % BK : -1;
   }
   if (a.pos_abs) a.pos_abs[b] = a.positions ? a.positions[b] : -1;
 }
 
-// one thread per (sequence, KV head, dimension)
+__global__ void __launch_bounds__(256) setup_kernel(SetupLaunch a) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b >= a.B) return;
+  const int32_t* frow = a.bt_full + static_cast<int64_t>(b) * a.bt_full_stride;
+  const int32_t* srow = a.bt_swa ? a.bt_swa + static_cast<int64_t>(b) * a.bt_swa_stride : nullptr;
+  setup_one(a, b, a.seq_lens[b], [&](int c) { return frow[c]; }, [&](int c) { return srow[c]; });
+}
+
+// Compressed page lists ("MPK Internals", "Phase 4": paged_kv_indptr,
+// paged_kv_indices, paged_kv_last_page_len): one workgroup per sequence
+// writes its token count and its padded full-table row, and its thread 0
+// builds the same control as setup_kernel.
+__global__ void __launch_bounds__(256) setup_csr_kernel(SetupLaunch a, CsrInput c) {
+  const int b = blockIdx.x;
+  const int lo = c.kv_indptr[b];
+  const int n = c.kv_indptr[b + 1] - lo;
+  const int len = n > 0 ? (n - 1) * a.block + c.last_page_len[b] : 0;
+  int32_t* frow = c.bt_full_out + static_cast<int64_t>(b) * a.bt_full_stride;
+  for (int i = threadIdx.x; i < a.bt_width; i += 256) frow[i] = i < n ? c.full_indices[lo + i] : -1;
+  if (threadIdx.x != 0) return;
+  c.seq_lens_out[b] = len;
+  setup_one(a, b, len, [&](int i) { return i < n ? c.full_indices[lo + i] : -1; },
+            [&](int i) { return i < n ? c.swa_indices[lo + i] : -1; });
+}
+
 __global__ void __launch_bounds__(256) kv_update_kernel(UpdateLaunch a) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const int64_t n = static_cast<int64_t>(a.B) * a.Hkv * kHeadDim;
@@ -81,6 +104,11 @@ __global__ void __launch_bounds__(256) kv_update_kernel(UpdateLaunch a) {
 hipError_t launch_setup(const SetupLaunch& L, hipStream_t stream) {
   const int n_wg = (L.B + 255) / 256;
   hipLaunchKernelGGL(setup_kernel, dim3(n_wg), dim3(256), 0, stream, L);
+  return hipGetLastError();
+}
+
+hipError_t launch_setup_csr(const SetupLaunch& L, const CsrInput& C, hipStream_t stream) {
+  hipLaunchKernelGGL(setup_csr_kernel, dim3(L.B), dim3(256), 0, stream, L, C);
   return hipGetLastError();
 }
 

@@ -59,6 +59,18 @@ struct SetupLaunch {
 };
 hipError_t launch_setup(const SetupLaunch& L, hipStream_t stream);
 
+// Compressed page lists for launch_setup_csr; the padded full table and the
+// token counts are outputs (SetupLaunch::bt_full / seq_lens unused).
+struct CsrInput {
+  const int32_t* kv_indptr;      // [B + 1]
+  const int32_t* full_indices;
+  const int32_t* swa_indices;    // null when window == 0
+  const int32_t* last_page_len;  // [B]
+  int32_t* bt_full_out;          // [B, bt_full_stride]
+  int32_t* seq_lens_out;         // [B]
+};
+hipError_t launch_setup_csr(const SetupLaunch& L, const CsrInput& C, hipStream_t stream);
+
 struct UpdateLaunch {
   int32_t B, Hkv, block;
   int64_t nb;
