@@ -20,7 +20,8 @@ Modules:
   layout     byte layout of one shared KV buffer, packed-K and plain-V addressing
   control    layer-invariant attention control (trimmed SWA table, positions,
              the two KV-update indices)
-  update     quantize-and-scatter of the new token's K/V
+  update     quantize-and-scatter of the new token's K/V (K optionally rotated)
+  rope       the rotary embedding of the new query and key (half-split pairing)
   attention  paged decode attention in float64 (plus a dense brute-force twin)
   step       the alternating SWA/full layer schedule over shared buffers
   budget     the KV-cache byte and block budget of a device (host policy)

@@ -23,7 +23,7 @@ import math
 
 import numpy as np
 
-from . import fp8_e4m3, layout
+from . import fp8_e4m3, layout, rope
 
 
 def gather_kv(k_half, v_half, table_row, lo: int, hi: int, head: int,
@@ -49,7 +49,8 @@ def key_range(frame_pos: int, window: int):
 
 def paged_decode_attention(q, k_half, v_half, block_table, frame_pos, window: int,
                            block: int, kv_heads: int, k_scale: float, v_scale: float,
-                           sm_scale: float, k_packed: bool = True, rows=None):
+                           sm_scale: float, k_packed: bool = True, rows=None,
+                           rope_cos=None, rope_sin=None):
     """Return out float64 [B, Hq, D].
 
     q          : [B, Hq, D] values (bf16 values held exactly in any float dtype)
@@ -57,8 +58,12 @@ def paged_decode_attention(q, k_half, v_half, block_table, frame_pos, window: in
     block_table: int [B, width] (full table, or the trimmed window table)
     frame_pos  : int [B], -1 for inactive
     rows       : optional iterable of sequence indices to compute (others stay 0)
+    rope_cos, rope_sin : optional [B, D/2] per-sequence rotation applied to
+                 every query head first (``rope.rotate``, float64)
     """
     q = np.asarray(q, dtype=np.float64)
+    if rope_cos is not None:
+        q = rope.rotate(q, np.asarray(rope_cos)[:, None, :], np.asarray(rope_sin)[:, None, :])
     B, Hq, D = q.shape
     G = Hq // kv_heads
     out = np.zeros((B, Hq, D), dtype=np.float64)

@@ -15,7 +15,8 @@ from . import attention, control, update
 
 def decode_step(buffers, q, k_new, v_new, seq_lens, active, bt_full, bt_swa,
                 block: int, kv_heads: int, window: int, k_scale, v_scale,
-                sm_scale: float, k_packed: bool = True, layers=None, kinds=None):
+                sm_scale: float, k_packed: bool = True, layers=None, kinds=None,
+                rope_cos=None, rope_sin=None):
     """Run ``len(q)`` layers in place on ``buffers``.
 
     buffers : list of (k_half, v_half) flat uint8 arrays, one pair per buffer.
@@ -25,6 +26,8 @@ def decode_step(buffers, q, k_new, v_new, seq_lens, active, bt_full, bt_swa,
               (writes are always done for every layer, in order).
     kinds   : optional per-layer list of "swa" / "full"; default is the
               alternating schedule (even layers sliding-window).
+    rope_cos, rope_sin : optional float32 [B, D/2]; the one rotation of this
+              step's queries and new keys, shared by every layer.
     Returns (outputs dict layer -> [B, Hq, D] float64, control dict).
     """
     ctl = control.attention_control(seq_lens, active, bt_full, bt_swa, block, window)
@@ -34,12 +37,13 @@ def decode_step(buffers, q, k_new, v_new, seq_lens, active, bt_full, bt_swa,
         swa = (i % 2 == 0) if kinds is None else (kinds[i] == "swa")
         slots = ctl["upd_swa"] if swa else ctl["upd_full"]
         update.kv_cache_update(k_half, v_half, np.asarray(k_new[i]), np.asarray(v_new[i]),
-                               slots, block, k_scale[i], v_scale[i], k_packed)
+                               slots, block, k_scale[i], v_scale[i], k_packed,
+                               rope_cos, rope_sin)
         if layers is not None and i not in layers:
             continue
         table = ctl["bt_swa_trim"] if swa else bt_full
         pos = ctl["pos_swa"] if swa else ctl["pos_full"]
         outs[i] = attention.paged_decode_attention(
             q[i], k_half, v_half, table, pos, window if swa else 0, block, kv_heads,
-            k_scale[i], v_scale[i], sm_scale, k_packed)
+            k_scale[i], v_scale[i], sm_scale, k_packed, rope_cos=rope_cos, rope_sin=rope_sin)
     return outs, ctl

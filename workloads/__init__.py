@@ -178,6 +178,22 @@ def make_workload(cfg: Config, hbm_bytes: int = None, swa_keep_blocks: int = Non
                     [cfg.k_scale] * nl, [cfg.v_scale] * nl, referenced)
 
 
+def rope_tables(wl: Workload, base: float = 10000.0):
+    """Per-sequence rotary cosines and sines for this step, float32 [B, D/2].
+
+    The pages carry cos/sin in the attention control but give no frequency
+    schedule; this draws them from the geometric schedule of the original
+    rotary-embedding paper (frequency i = base^(-2i/D)) at each sequence's
+    absolute position, angles in float64, then rounded to float32.  Large
+    absolute positions (the offset workload) give angles far from zero, so
+    every quadrant and both signs of cos/sin occur.
+    """
+    D = wl.cfg.head_dim
+    inv = base ** (-2.0 * np.arange(D // 2, dtype=np.float64) / D)
+    ang = wl.positions.astype(np.float64)[:, None] * inv[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
 def _codes_like_normal(n: int, scale: float, gen: torch.Generator, device) -> torch.Tensor:
     x = torch.randn(n, generator=gen, device=device, dtype=torch.float32)
     return x.div_(scale).to(torch.float8_e4m3fn).view(torch.uint8)
