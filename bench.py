@@ -118,6 +118,8 @@ def main():
                     help="block tables as padded rows (default) or compressed page lists")
     ap.add_argument("--k-layout", choices=["packed", "unpacked"], default="packed",
                     help="K half arrangement: packed token pairs (default) or token-major rows")
+    ap.add_argument("--rope", action="store_true",
+                    help="turn the queries and new keys by per-sequence rotary cos/sin")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -151,6 +153,10 @@ def main():
     q, k_new, v_new = wl.q.to(dev), wl.k_new.to(dev), wl.v_new.to(dev)
     has_swa = "swa" in cfg.kinds
     win = cfg.window if has_swa else 0
+    rkw = {}
+    if args.rope:
+        rc, rs = W.rope_tables(wl)
+        rkw = dict(rope_cos=to(rc), rope_sin=to(rs))
     if args.tables == "csr":
         # the same tables as compressed page lists; the setup writes the padded
         # full table the layers read
@@ -186,7 +192,8 @@ def main():
     alternating = all(k == ("swa" if i % 2 == 0 else "full") for i, k in enumerate(cfg.kinds))
     kp = args.k_layout == "packed"
     step_desc = P.make_step(bufs, ctl, bt_full, cfg.batch, cfg.hq, cfg.hkv, cfg.head_dim,
-                            cfg.block, cfg.window, wl.nb, k_packed=kp) if alternating else None
+                            cfg.block, cfg.window, wl.nb, k_packed=kp,
+                            **rkw) if alternating else None
 
     def attn(i):
         swa = cfg.kinds[i] == "swa"
@@ -194,17 +201,17 @@ def main():
         if swa:
             P.pkv_paged_decode_attn(q[i], buf, ctl["bt_swa_trim"], ctl["pos_swa"], cfg.block,
                                     wl.nb, cfg.window, wl.k_scale[i], wl.v_scale[i], sm, cfg.hkv,
-                                    out=outs[i], workspace=ws_swa, k_packed=kp)
+                                    out=outs[i], workspace=ws_swa, k_packed=kp, **rkw)
         else:
             P.pkv_paged_decode_attn(q[i], buf, bt_full, ctl["pos_full"], cfg.block, wl.nb, 0,
                                     wl.k_scale[i], wl.v_scale[i], sm, cfg.hkv, out=outs[i],
-                                    workspace=ws_full, k_packed=kp)
+                                    workspace=ws_full, k_packed=kp, **rkw)
 
     def update(i):
         swa = cfg.kinds[i] == "swa"
         P.pkv_kv_cache_update(bufs[i // 2], k_new[i], v_new[i],
                               ctl["upd_swa"] if swa else ctl["upd_full"], cfg.block, wl.nb,
-                              wl.k_scale[i], wl.v_scale[i], k_packed=kp)
+                              wl.k_scale[i], wl.v_scale[i], k_packed=kp, **rkw)
 
     def layer(i):
         if step_desc is not None:
@@ -295,7 +302,7 @@ def main():
     if os.path.exists(TRAFFIC_FILE):
         tr = json.load(open(TRAFFIC_FILE))
         if (tr.get("kernel_sha") == kernel_sha() and tr.get("config") == args.config
-                and args.k_layout == "packed" and args.tables == "padded"):
+                and args.k_layout == "packed" and args.tables == "padded" and not args.rope):
             traffic = tr.get("bytes_per_launch")
     value = step_bytes / (ms * 1e-3) / 1e9
     result = {
@@ -315,7 +322,7 @@ def main():
                    "q_heads": cfg.hq, "kv_heads": cfg.hkv, "head_dim": cfg.head_dim,
                    "block": cfg.block, "context": "8192" if cfg.ctx[0] == "fixed" else str(cfg.ctx),
                    "window": cfg.window, "num_blocks": wl.nb, "k_layout": args.k_layout, "tables": args.tables,
-                   "graph": use_graph},
+                   "rope": args.rope, "graph": use_graph},
         "tokens_per_s": round(cfg.batch / (ms * 1e-3), 1),
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
         "kv_bytes_per_step": step_bytes,

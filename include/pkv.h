@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 1
+#define PKV_ABI_VERSION 2
 
 typedef enum {
   PKV_OK = 0,
@@ -155,11 +155,18 @@ int pkv_setup_attn_control_csr(int32_t batch, int32_t block, int32_t window,
  * 16-byte aligned).  k_packed != 0 selects the packed K arrangement.
  * slot_idx int64 [batch]: block_id*block + offset, -1 = no write; slots outside
  * [0, num_blocks*block) are skipped.  Stored code = E4M3(fp32(x) / scale)
- * rounded to nearest even, saturating to +-448, NaN -> 0x7F|sign. */
+ * rounded to nearest even, saturating to +-448, NaN -> 0x7F|sign.
+ * rope_cos, rope_sin: fp32 [batch, head_dim/2] (4-byte aligned) or both NULL.
+ * Given, K is first turned by the attention control's rotary cos/sin
+ * ("Kernel contract"), half-split: with h = head_dim/2 and i < h,
+ * x_i' = x_i*c_i - x_{i+h}*s_i and x_{i+h}' = x_{i+h}*c_i + x_i*s_i, each
+ * product rounded to fp32 before the sum (no fused multiply-add); x' is then
+ * quantised as above.  V is never turned. */
 int pkv_kv_cache_update(int32_t batch, int32_t kv_heads, int32_t head_dim, int32_t block,
                         int64_t num_blocks, const uint16_t* k_new, const uint16_t* v_new,
                         uint8_t* k_half, int32_t k_packed, uint8_t* v_half,
-                        const int64_t* slot_idx, float k_scale, float v_scale, void* stream);
+                        const int64_t* slot_idx, const float* rope_cos, const float* rope_sin,
+                        float k_scale, float v_scale, void* stream);
 
 /* Device bytes of the workspace pkv_paged_decode_attn needs for these shapes
  * (split-KV partial results and per-(sequence, KV head) arrival counters).
@@ -187,6 +194,10 @@ int64_t pkv_decode_workspace_bytes(int32_t batch, int32_t q_heads, int32_t kv_he
  * k_packed: 1 = the K half in the packed view [nb, Hkv, block/2, head_dim, 2]
  * (two tokens interleaved per dimension), 0 = token-major rows
  * [nb, Hkv, block, head_dim] like V ("KV-cache layout"); same bytes, same speed.
+ * rope_cos, rope_sin: fp32 [batch, head_dim/2] (16-byte aligned) or both NULL;
+ * given, every query head of sequence b is first turned half-split by row b
+ * (as in pkv_kv_cache_update), in fp32 and rounded to bf16 for the scores.
+ * The cached keys are used as stored (a writer turned them before caching).
  * workspace: at least pkv_decode_workspace_bytes(...) bytes, 256-byte aligned,
  * zero-filled before first use. */
 int pkv_paged_decode_attn(int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t head_dim,
@@ -194,6 +205,7 @@ int pkv_paged_decode_attn(int32_t batch, int32_t q_heads, int32_t kv_heads, int3
                           const uint16_t* q, const uint8_t* k_half, int32_t k_packed,
                           const uint8_t* v_half, const int32_t* block_table, int32_t bt_stride,
                           int32_t table_width, const int32_t* frame_pos,
+                          const float* rope_cos, const float* rope_sin,
                           float k_scale, float v_scale, float sm_scale, uint16_t* out,
                           void* workspace, int64_t workspace_bytes, void* stream);
 
@@ -220,6 +232,8 @@ typedef struct pkv_step {
   const int32_t* pos_swa;
   const int64_t* upd_full;
   const int64_t* upd_swa;
+  const float* rope_cos;        /* fp32 [batch, head_dim/2] rotary cos/sin of the */
+  const float* rope_sin;        /* step (16-byte aligned), or both NULL          */
 } pkv_step;
 
 /* One layer of the alternating schedule ("Kernel contract"): layer i writes
@@ -234,7 +248,9 @@ typedef struct pkv_step {
  * upd_swa / upd_full name when the control comes from pkv_setup_attn_control,
  * which is this entry point's precondition -- and attends to it.  Buffer
  * bytes and outputs are identical to pkv_kv_cache_update followed by
- * pkv_paged_decode_attn.  No id outside [0, num_blocks) is written.  The
+ * pkv_paged_decode_attn (with the step's rope_cos / rope_sin passed to both
+ * when given: the new K is turned before it is quantised, every query head
+ * before the scores).  No id outside [0, num_blocks) is written.  The
  * block holding a sequence's new token must not appear in another sequence's
  * table of the same layer (its old bytes could be read there). */
 int pkv_decode_layer(const pkv_step* step, int32_t layer, const uint16_t* q,

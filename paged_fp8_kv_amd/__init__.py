@@ -40,7 +40,7 @@ class PkvStep(ctypes.Structure):
         ("k_packed", _i32), ("k_bufs", ctypes.POINTER(_vp)), ("v_bufs", ctypes.POINTER(_vp)),
         ("stacked", _vp), ("bt_full", _vp), ("bt_full_stride", _i32), ("bt_full_width", _i32),
         ("bt_swa_trim", _vp), ("trim_width", _i32), ("pos_full", _vp), ("pos_swa", _vp),
-        ("upd_full", _vp), ("upd_swa", _vp),
+        ("upd_full", _vp), ("upd_swa", _vp), ("rope_cos", _vp), ("rope_sin", _vp),
     ]
 
 
@@ -57,10 +57,11 @@ _SIGS = {
     "pkv_setup_attn_control_csr": ([_i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
                                     _i32, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp], _i32),
     "pkv_kv_cache_update": ([_i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _i32, _vp, _vp,
-                             _f32, _f32, _vp], _i32),
+                             _vp, _vp, _f32, _f32, _vp], _i32),
     "pkv_decode_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32, _i32, _i32], _i64),
     "pkv_paged_decode_attn": ([_i32, _i32, _i32, _i32, _i32, _i64, _i32, _vp, _vp, _i32, _vp,
-                               _vp, _i32, _i32, _vp, _f32, _f32, _f32, _vp, _vp, _i64, _vp], _i32),
+                               _vp, _i32, _i32, _vp, _vp, _vp, _f32, _f32, _f32, _vp, _vp, _i64,
+                               _vp], _i32),
     "pkv_decode_layer": ([ctypes.POINTER(PkvStep), _i32, _vp, _vp, _vp, _f32, _f32, _f32, _vp,
                           _vp, _i64, _vp], _i32),
     "pkv_validate_attn_control": ([_i32, _i32, _i32, _i64, _vp, _vp, _vp, _i32, _vp, _i32,
@@ -68,6 +69,7 @@ _SIGS = {
 }
 
 _lib = None
+ABI_VERSION = 2  # PKV_ABI_VERSION these signatures follow
 
 
 def lib():
@@ -80,6 +82,9 @@ def lib():
         for name, (args, res) in _SIGS.items():
             f = getattr(L, name)
             f.argtypes, f.restype = args, res
+        if L.pkv_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} has ABI {L.pkv_abi_version()}, the binding expects "
+                               f"{ABI_VERSION}: rebuild with `python -m paged_fp8_kv_amd.build`")
         _lib = L
     return _lib
 
@@ -219,15 +224,28 @@ def pkv_setup_attn_control_csr(kv_indptr, full_indices, swa_indices, last_page_l
     return out
 
 
+def _rope(rope_cos, rope_sin, batch, head_dim):
+    """Device pointers of the per-sequence rotary cos/sin (float32 [B, D/2]) or (None, None)."""
+    if rope_cos is None and rope_sin is None:
+        return None, None
+    for t, n in ((rope_cos, "rope_cos"), (rope_sin, "rope_sin")):
+        if t is None or tuple(t.shape) != (batch, head_dim // 2):
+            raise ValueError(f"{n} must be float32 [{batch}, {head_dim // 2}]")
+    return (_dev_ptr(rope_cos, torch.float32, "rope_cos"),
+            _dev_ptr(rope_sin, torch.float32, "rope_sin"))
+
+
 def pkv_kv_cache_update(buf, k_new, v_new, slot_idx, block, num_blocks, k_scale, v_scale,
-                        k_packed=True, stream=None):
-    """buf: one shared buffer (uint8, K half then V half); k_new/v_new bf16 [B, Hkv, D]."""
+                        k_packed=True, stream=None, rope_cos=None, rope_sin=None):
+    """buf: one shared buffer (uint8, K half then V half); k_new/v_new bf16 [B, Hkv, D];
+    rope_cos/rope_sin: optional float32 [B, D/2] rotation of K."""
     B, H, D = k_new.shape
     kp, vp = _halves(buf, num_blocks, H, block, D)
+    rc, rs = _rope(rope_cos, rope_sin, B, D)
     _check(lib().pkv_kv_cache_update(
         B, H, D, block, num_blocks, _dev_ptr(k_new, torch.bfloat16, "k_new"),
         _dev_ptr(v_new, torch.bfloat16, "v_new"), kp, int(bool(k_packed)), vp,
-        _dev_ptr(slot_idx, torch.int64, "slot_idx"), float(k_scale), float(v_scale),
+        _dev_ptr(slot_idx, torch.int64, "slot_idx"), rc, rs, float(k_scale), float(v_scale),
         _stream(stream)))
 
 
@@ -244,9 +262,12 @@ def new_workspace(batch, q_heads, kv_heads, head_dim, block, table_width, window
 
 def pkv_paged_decode_attn(q, buf, block_table, frame_pos, block, num_blocks, window, k_scale,
                           v_scale, sm_scale, kv_heads, table_width=None, out=None,
-                          workspace=None, k_packed=True, stream=None):
-    """q bf16 [B, Hq, D]; returns out bf16 [B, Hq, D]."""
+                          workspace=None, k_packed=True, stream=None, rope_cos=None,
+                          rope_sin=None):
+    """q bf16 [B, Hq, D]; returns out bf16 [B, Hq, D].  rope_cos/rope_sin: optional
+    float32 [B, D/2] rotation of the queries."""
     B, Hq, D = q.shape
+    rc, rs = _rope(rope_cos, rope_sin, B, D)
     kp, vp = _halves(buf, num_blocks, kv_heads, block, D)
     width = block_table.shape[1] if table_width is None else table_width
     if out is None:
@@ -256,16 +277,17 @@ def pkv_paged_decode_attn(q, buf, block_table, frame_pos, block, num_blocks, win
     _check(lib().pkv_paged_decode_attn(
         B, Hq, kv_heads, D, block, num_blocks, window, _dev_ptr(q, torch.bfloat16, "q"), kp,
         int(bool(k_packed)), vp, _dev_ptr(block_table, torch.int32, "block_table"),
-        block_table.shape[1], width, _dev_ptr(frame_pos, torch.int32, "frame_pos"),
+        block_table.shape[1], width, _dev_ptr(frame_pos, torch.int32, "frame_pos"), rc, rs,
         float(k_scale), float(v_scale), float(sm_scale), _dev_ptr(out, torch.bfloat16, "out"),
         _dev_ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
     return out
 
 
 def make_step(bufs, ctl, bt_full, batch, q_heads, kv_heads, head_dim, block, window,
-              num_blocks, k_packed=True, stacked=None):
+              num_blocks, k_packed=True, stacked=None, rope_cos=None, rope_sin=None):
     """Host pkv_step for the layer schedule.  bufs: list of shared buffers (per-buffer
-    form) or None with `stacked` (one uint8 tensor of consecutive buffers)."""
+    form) or None with `stacked` (one uint8 tensor of consecutive buffers);
+    rope_cos/rope_sin: optional float32 [batch, head_dim/2] rotation of the step."""
     s = PkvStep()
     s.batch, s.q_heads, s.kv_heads, s.head_dim = batch, q_heads, kv_heads, head_dim
     s.block, s.window, s.num_blocks = block, window, num_blocks
@@ -293,6 +315,8 @@ def make_step(bufs, ctl, bt_full, batch, q_heads, kv_heads, head_dim, block, win
     s.pos_swa = ctl["pos_swa"].data_ptr()
     s.upd_full = ctl["upd_full"].data_ptr()
     s.upd_swa = ctl["upd_swa"].data_ptr()
+    s.rope_cos, s.rope_sin = _rope(rope_cos, rope_sin, batch, head_dim)
+    keep += [rope_cos, rope_sin]
     s._keep = keep
     return s
 

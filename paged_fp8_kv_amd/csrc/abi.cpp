@@ -212,7 +212,8 @@ int pkv_setup_attn_control_csr(int32_t batch, int32_t block, int32_t window,
 int pkv_kv_cache_update(int32_t batch, int32_t kv_heads, int32_t head_dim, int32_t block,
                         int64_t num_blocks, const uint16_t* k_new, const uint16_t* v_new,
                         uint8_t* k_half, int32_t k_packed, uint8_t* v_half,
-                        const int64_t* slot_idx, float k_scale, float v_scale, void* stream) {
+                        const int64_t* slot_idx, const float* rope_cos, const float* rope_sin,
+                        float k_scale, float v_scale, void* stream) {
   if (batch < 0) return fail(PKV_ERR_ARG, "batch must be >= 0");
   if (batch == 0) return ok();
   int st = check_kv_shape(kv_heads, head_dim, block, num_blocks);
@@ -222,6 +223,10 @@ int pkv_kv_cache_update(int32_t batch, int32_t kv_heads, int32_t head_dim, int32
   if (!aligned(k_half, 16) || !aligned(v_half, 16))
     return fail(PKV_ERR_ARG, "K/V halves must be 16-byte aligned");
   if (k_packed != 0 && k_packed != 1) return fail(PKV_ERR_ARG, "k_packed must be 0 or 1");
+  if ((rope_cos == nullptr) != (rope_sin == nullptr))
+    return fail(PKV_ERR_ARG, "rope_cos and rope_sin must both be given or both be null");
+  if (rope_cos && (!aligned(rope_cos, 4) || !aligned(rope_sin, 4)))
+    return fail(PKV_ERR_ARG, "rope_cos / rope_sin must be 4-byte aligned");
   if (!(k_scale > 0.f) || !(v_scale > 0.f) || k_scale == INFINITY || v_scale == INFINITY)
     return fail(PKV_ERR_ARG, "scales must be finite and > 0");
   pkv::UpdateLaunch L{};
@@ -237,6 +242,8 @@ int pkv_kv_cache_update(int32_t batch, int32_t kv_heads, int32_t head_dim, int32
   L.slot = slot_idx;
   L.k_scale = k_scale;
   L.v_scale = v_scale;
+  L.rope_cos = rope_cos;
+  L.rope_sin = rope_sin;
   return hip_status(pkv::launch_kv_update(L, static_cast<hipStream_t>(stream)), "kv update launch");
 }
 
@@ -262,7 +269,8 @@ static int attn_impl(int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t h
                      const int32_t* block_table, int32_t bt_stride, int32_t table_width,
                      const int32_t* frame_pos, float k_scale, float v_scale, float sm_scale,
                      uint16_t* out, void* workspace, int64_t workspace_bytes, void* stream,
-                     const uint16_t* k_new, const uint16_t* v_new, uint8_t* k_w, uint8_t* v_w) {
+                     const uint16_t* k_new, const uint16_t* v_new, uint8_t* k_w, uint8_t* v_w,
+                     const float* rope_cos, const float* rope_sin) {
   if (batch < 0) return fail(PKV_ERR_ARG, "batch must be >= 0");
   if (batch == 0) return ok();
   if (batch > pkv::kMaxBatch)
@@ -286,6 +294,10 @@ static int attn_impl(int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t h
   if (!aligned(block_table, 4) || !aligned(frame_pos, 4))
     return fail(PKV_ERR_ARG, "tables must be 4-byte aligned");
   if (k_packed != 0 && k_packed != 1) return fail(PKV_ERR_ARG, "k_packed must be 0 or 1");
+  if ((rope_cos == nullptr) != (rope_sin == nullptr))
+    return fail(PKV_ERR_ARG, "rope_cos and rope_sin must both be given or both be null");
+  if (rope_cos && (!aligned(rope_cos, 16) || !aligned(rope_sin, 16)))
+    return fail(PKV_ERR_ARG, "rope_cos / rope_sin must be 16-byte aligned");
   if (!(k_scale > 0.f) || !(v_scale > 0.f) || !(sm_scale > 0.f) || k_scale == INFINITY ||
       v_scale == INFINITY || sm_scale == INFINITY)
     return fail(PKV_ERR_ARG, "scales must be finite and > 0");
@@ -321,6 +333,8 @@ static int attn_impl(int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t h
   L.v_new = v_new;
   L.k_w = k_w;
   L.v_w = v_w;
+  L.rope_cos = rope_cos;
+  L.rope_sin = rope_sin;
   return hip_status(pkv::launch_decode_attn(L, static_cast<hipStream_t>(stream)), "attention launch");
 }
 
@@ -328,12 +342,13 @@ int pkv_paged_decode_attn(int32_t batch, int32_t q_heads, int32_t kv_heads, int3
                           int32_t block, int64_t num_blocks, int32_t window, const uint16_t* q,
                           const uint8_t* k_half, int32_t k_packed, const uint8_t* v_half,
                           const int32_t* block_table, int32_t bt_stride, int32_t table_width,
-                          const int32_t* frame_pos, float k_scale, float v_scale, float sm_scale,
+                          const int32_t* frame_pos, const float* rope_cos,
+                          const float* rope_sin, float k_scale, float v_scale, float sm_scale,
                           uint16_t* out, void* workspace, int64_t workspace_bytes, void* stream) {
   return attn_impl(batch, q_heads, kv_heads, head_dim, block, num_blocks, window, q, k_half,
                    k_packed, v_half, block_table, bt_stride, table_width, frame_pos, k_scale,
                    v_scale, sm_scale, out, workspace, workspace_bytes, stream, nullptr, nullptr,
-                   nullptr, nullptr);
+                   nullptr, nullptr, rope_cos, rope_sin);
 }
 
 int pkv_decode_layer(const pkv_step* s, int32_t layer, const uint16_t* q, const uint16_t* k_new,
@@ -372,11 +387,11 @@ int pkv_decode_layer(const pkv_step* s, int32_t layer, const uint16_t* q, const 
     return attn_impl(s->batch, s->q_heads, s->kv_heads, s->head_dim, s->block, s->num_blocks,
                      s->window, q, kh, s->k_packed, vh, s->bt_swa_trim, s->trim_width,
                      s->trim_width, s->pos_swa, k_scale, v_scale, sm_scale, out, workspace,
-                     workspace_bytes, stream, k_new, v_new, kh, vh);
+                     workspace_bytes, stream, k_new, v_new, kh, vh, s->rope_cos, s->rope_sin);
   return attn_impl(s->batch, s->q_heads, s->kv_heads, s->head_dim, s->block, s->num_blocks, 0, q,
                    kh, s->k_packed, vh, s->bt_full, s->bt_full_stride, s->bt_full_width,
                    s->pos_full, k_scale, v_scale, sm_scale, out, workspace, workspace_bytes, stream,
-                   k_new, v_new, kh, vh);
+                   k_new, v_new, kh, vh, s->rope_cos, s->rope_sin);
 }
 
 int pkv_validate_attn_control(int32_t batch, int32_t block, int32_t window, int64_t num_blocks,

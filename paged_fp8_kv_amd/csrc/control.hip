@@ -5,7 +5,8 @@
 // trimmed sliding-window table, the absolute and window-frame positions and
 // the two KV-update indices.  The KV write quantises the new token's K/V to
 // OCP E4M3 and scatters them through an update index, K through the packed
-// view and V plain ("KV-cache layout").
+// view and V plain ("KV-cache layout"); with the control's rotary cos/sin it
+// turns K (half-split) in fp32 first.
 #include "pkv_device.hpp"
 #include "pkv_internal.hpp"
 
@@ -90,7 +91,14 @@ __global__ void __launch_bounds__(256) kv_update_kernel(UpdateLaunch a) {
   if (slot < 0 || slot >= a.nb * BK) return;
   const int64_t blk = slot / BK;
   const int t = static_cast<int>(slot % BK);
-  const float kx = __fdiv_rn(bf16_bits_to_f32(a.k_new[idx]), a.k_scale);
+  float kf = bf16_bits_to_f32(a.k_new[idx]);
+  if (a.rope_cos != nullptr) {
+    // partner dimension j ^ 32 of the same row (rows are 64-aligned)
+    const int i = b * (kHeadDim / 2) + (j & (kHeadDim / 2 - 1));
+    kf = rope_turn(kf, bf16_bits_to_f32(a.k_new[idx ^ (kHeadDim / 2)]), a.rope_cos[i],
+                   a.rope_sin[i], j >= kHeadDim / 2);
+  }
+  const float kx = __fdiv_rn(kf, a.k_scale);
   const float vx = __fdiv_rn(bf16_bits_to_f32(a.v_new[idx]), a.v_scale);
   const int64_t tile = (blk * a.Hkv + h) * static_cast<int64_t>(BK) * kHeadDim;
   const int64_t koff = a.k_packed ? tile + (static_cast<int64_t>(t / 2) * kHeadDim + j) * 2 + (t & 1)

@@ -80,6 +80,9 @@ struct AttnArgs {
   uint8_t* k_w;
   uint8_t* v_w;
   float k_scale;
+  // rotary cos/sin fp32 [B, 32] (null: none) for the queries and the new K
+  const float* rope_cos;
+  const float* rope_sin;
 };
 
 // frame range [lo, hi] of sequence b; returns the number of sub-tiles
@@ -645,11 +648,37 @@ __device__ __forceinline__ int64_t first_item_start_at_or_after(const int* s_pre
   return static_cast<int64_t>(s_pre[lo_i + 1]) * hkv;  // first item of the next sequence with work
 }
 
+// Half-split rotation of the lane's 16 query dims (16q .. 16q+15, packed bf16
+// in q0, q1); the partner dims 16(q^2) .. live in lane ^ 32.  fp32, then
+// rounded to bf16 for the score MFMA.
+__device__ __forceinline__ void rotate_queries(u32x4_t& q0, u32x4_t& q1, const f32x4_t (&c)[4],
+                                               const f32x4_t (&s)[4], bool upper) {
+  uint32_t w[8] = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
+  uint32_t p[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) p[k] = static_cast<uint32_t>(__shfl_xor(static_cast<int>(w[k]), 32));
+  uint32_t r[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    uint32_t lohi[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int d = 2 * k + e;
+      const float x = __uint_as_float((e ? w[k] & 0xffff0000u : w[k] << 16));
+      const float xp = __uint_as_float((e ? p[k] & 0xffff0000u : p[k] << 16));
+      lohi[e] = f32_to_bf16_bits(rope_turn(x, xp, c[d >> 2][d & 3], s[d >> 2][d & 3], upper));
+    }
+    r[k] = lohi[0] | (lohi[1] << 16);
+  }
+  q0 = u32x4_t{r[0], r[1], r[2], r[3]};
+  q1 = u32x4_t{r[4], r[5], r[6], r[7]};
+}
+
 // Process the sub-tiles [cur, wend) of the item line, chunk `cid` of the
 // schedule.  Items that lie wholly inside are written out; pieces of items
 // cut by chunk boundaries go through partial slots 2*cid / 2*cid+1 and are
 // merged by the last piece to arrive.
-template <int BK, bool WINDOWED, bool KP>
+template <int BK, bool WINDOWED, bool KP, bool ROPE>
 __device__ __forceinline__ void process_chunk(const AttnArgs& a, const int* s_pre, int B, int cid,
                                               const Sched sc, int64_t cur, int64_t wend,
                                               uint8_t* ring) {
@@ -690,19 +719,37 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const int* s_pr
       q0 = *reinterpret_cast<const u32x4_t*>(qp);
       q1 = *reinterpret_cast<const u32x4_t*>(qp + 8);
     }
+    // rotary cos/sin of the lane's dims 16q .. 16q+15 (frequencies 16(q&1) ..)
+    f32x4_t rc[4], rs[4];
+    constexpr bool rope = ROPE;
+    if (rope) {
+      const int64_t ro = static_cast<int64_t>(b) * (kHeadDim / 2) + 16 * (q & 1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        rc[i] = *reinterpret_cast<const f32x4_t*>(a.rope_cos + ro + 4 * i);
+        rs[i] = *reinterpret_cast<const f32x4_t*>(a.rope_sin + ro + 4 * i);
+      }
+    }
     // the new token's K/V rows (fused write), fetched with the queries; used
     // only by the segment holding the token
     uint16_t kn_bits = 0, vn_bits = 0;
+    float kn_c = 1.f, kn_s = 0.f;
     if (a.k_new != nullptr) {
       const int64_t row = (static_cast<int64_t>(b) * a.Hkv + h) * kHeadDim + lane;
       kn_bits = a.k_new[row];
       vn_bits = a.v_new[row];
+      if (rope) {
+        const int64_t ci = static_cast<int64_t>(b) * (kHeadDim / 2) + (lane & (kHeadDim / 2 - 1));
+        kn_c = a.rope_cos[ci];
+        kn_s = a.rope_sin[ci];
+      }
     }
     const int hi = __builtin_amdgcn_readfirstlane(fp_raw);
     const int lo = WINDOWED ? max(0, hi - a.window + 1) : 0;
     it.set_range(lo, hi);
     if (WINDOWED) it.load_window(it.clampc(((lo / kSub + j) * kSub) / BK));
 
+    if (rope) rotate_queries(q0, q1, rc, rs, q >= 2);
     // expanded queries: qx[i][k] holds q[g][16q + 4i + k] in the half of parity e
     uint32_t qx[4][4];
     {
@@ -725,7 +772,11 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const int* s_pr
                        hi / kSub < lo / kSub + j + seg) ? hi / kSub : -1;
     uint32_t kcode = 0, vcode = 0;
     if (t_new >= 0) {
-      kcode = f32_to_e4m3_rne_sat(__fdiv_rn(bf16_bits_to_f32(kn_bits), a.k_scale));
+      float kf = bf16_bits_to_f32(kn_bits);
+      if (rope)  // partner dimension lane ^ 32 (t_new is uniform: every lane is here)
+        kf = rope_turn(kf, bf16_bits_to_f32(static_cast<uint16_t>(__shfl_xor(static_cast<int>(kn_bits), 32))),
+                       kn_c, kn_s, lane >= kHeadDim / 2);
+      kcode = f32_to_e4m3_rne_sat(__fdiv_rn(kf, a.k_scale));
       vcode = f32_to_e4m3_rne_sat(__fdiv_rn(bf16_bits_to_f32(vn_bits), a.v_scale));
     }
     State s;
@@ -833,7 +884,7 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const int* s_pr
   }
 }
 
-template <int BK, bool WINDOWED, bool KP>
+template <int BK, bool WINDOWED, bool KP, bool ROPE>
 __global__ void __launch_bounds__(kThreads, kWGPerCU * kWavesPerWG / 4) decode_attn_kernel(AttnArgs a) {
   extern __shared__ int s_pre[];  // [B + 1] prefix of per-sequence sub-tile counts
   __shared__ int s_longest;       // longest item, in sub-tiles
@@ -884,23 +935,35 @@ __global__ void __launch_bounds__(kThreads, kWGPerCU * kWavesPerWG / 4) decode_a
   if (longest_item <= kTinyItem || 2 * static_cast<int64_t>(longest_item) <= per) {
     const int64_t lo_w = first_item_start_at_or_after(s_pre, B, a.Hkv, cb);
     const int64_t hi_w = first_item_start_at_or_after(s_pre, B, a.Hkv, min(cb + per, total));
-    if (lo_w < hi_w) process_chunk<BK, WINDOWED, KP>(a, s_pre, B, wid, sc, lo_w, hi_w, ring);
+    if (lo_w < hi_w) process_chunk<BK, WINDOWED, KP, ROPE>(a, s_pre, B, wid, sc, lo_w, hi_w, ring);
   } else {
-    process_chunk<BK, WINDOWED, KP>(a, s_pre, B, wid, sc, cb, min(cb + per, total), ring);
+    process_chunk<BK, WINDOWED, KP, ROPE>(a, s_pre, B, wid, sc, cb, min(cb + per, total), ring);
   }
   wait_vmcnt<0>();  // no direct-to-LDS load outlives the wave
 }
 
-template <int BK, bool WINDOWED, bool KP>
+template <int BK, bool WINDOWED, bool KP, bool ROPE>
 hipError_t launch(const AttnArgs& a, int n_wg, size_t lds, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_attn_kernel<BK, WINDOWED, KP>), dim3(n_wg), dim3(kThreads), lds, stream, a);
+  hipLaunchKernelGGL((decode_attn_kernel<BK, WINDOWED, KP, ROPE>), dim3(n_wg), dim3(kThreads), lds,
+                     stream, a);
   return hipGetLastError();
 }
 
+template <int BK, bool ROPE>
+hipError_t launch_kp(const AttnArgs& a, bool win, bool kp, int n_wg, size_t lds, hipStream_t stream) {
+  if (kp)
+    return win ? launch<BK, true, true, ROPE>(a, n_wg, lds, stream)
+               : launch<BK, false, true, ROPE>(a, n_wg, lds, stream);
+  return win ? launch<BK, true, false, ROPE>(a, n_wg, lds, stream)
+             : launch<BK, false, false, ROPE>(a, n_wg, lds, stream);
+}
+
+// The rotary variant is a separate instantiation so that calls without it run
+// the kernel without its code.
 template <int BK>
 hipError_t launch_bk(const AttnArgs& a, bool win, bool kp, int n_wg, size_t lds, hipStream_t stream) {
-  if (kp) return win ? launch<BK, true, true>(a, n_wg, lds, stream) : launch<BK, false, true>(a, n_wg, lds, stream);
-  return win ? launch<BK, true, false>(a, n_wg, lds, stream) : launch<BK, false, false>(a, n_wg, lds, stream);
+  return a.rope_cos != nullptr ? launch_kp<BK, true>(a, win, kp, n_wg, lds, stream)
+                               : launch_kp<BK, false>(a, win, kp, n_wg, lds, stream);
 }
 
 }  // namespace
@@ -957,6 +1020,8 @@ hipError_t launch_decode_attn(const AttnLaunch& L, hipStream_t stream) {
   a.k_scale = L.k_scale;
   a.k_new = L.k_new;
   a.v_new = L.v_new;
+  a.rope_cos = L.rope_cos;
+  a.rope_sin = L.rope_sin;
   a.k_w = L.k_w;
   a.v_w = L.v_w;
   a.n_workers = L.n_workers;

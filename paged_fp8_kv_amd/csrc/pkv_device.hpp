@@ -28,6 +28,19 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// Half-split rotary turn of one element: x at dimension d, xp its partner at
+// d ^ (D/2), `upper` when d >= D/2, (c, s) the cosine and sine of the pair's
+// angle.  The lower element becomes x*c - xp*s, the upper one x*c + xp*s
+// (the pair, as x_lo + j*x_hi, times c + j*s).  Each product is rounded to
+// fp32 before the sum (contraction off), so the value -- and an FP8 code
+// taken from it -- is one defined fp32 result.
+__device__ __forceinline__ float rope_turn(float x, float xp, float c, float s, bool upper) {
+#pragma clang fp contract(off)
+  const float xc = x * c;
+  const float ps = xp * s;
+  return upper ? xc + ps : xc - ps;
+}
+
 // OCP E4M3 code of an fp32 value: round to nearest, ties to the even code,
 // |y| >= 448 (and +-inf) saturate to 0x7E|sign, NaN -> 0x7F|sign.
 // Positive codes 0x00..0x7E are monotone in value with a carry-continuous

@@ -33,6 +33,10 @@ struct AttnLaunch {
   const uint16_t* v_new;
   uint8_t* k_w;
   uint8_t* v_w;
+  // Optional rotary cos/sin, fp32 [B, 32] (null: no rotation): every query
+  // head, and the new K before it is quantised, are turned half-split.
+  const float* rope_cos;
+  const float* rope_sin;
 };
 
 int attn_max_subtiles(int block, int table_width, int window);
@@ -81,6 +85,8 @@ struct UpdateLaunch {
   int32_t k_packed;
   const int64_t* slot;
   float k_scale, v_scale;
+  const float* rope_cos;  // fp32 [B, 32] or null: K rotated before quantising
+  const float* rope_sin;
 };
 hipError_t launch_kv_update(const UpdateLaunch& L, hipStream_t stream);
 

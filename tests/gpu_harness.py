@@ -72,10 +72,13 @@ def device_inputs(wl, dev):
                 v_new=wl.v_new.to(dev))
 
 
-def gpu_step(wl, bufs, dev, use_layer_api=True, workspaces=None, k_packed=True):
-    """Run setup + every layer on the GPU; returns (outputs list, control dict)."""
+def gpu_step(wl, bufs, dev, use_layer_api=True, workspaces=None, k_packed=True, rope=None):
+    """Run setup + every layer on the GPU; returns (outputs list, control dict).
+    rope: optional (cos, sin) float32 numpy [B, D/2] rotation of the step."""
     c = wl.cfg
     d = device_inputs(wl, dev)
+    rc, rs = (None, None) if rope is None else (torch.from_numpy(rope[0]).to(dev),
+                                                 torch.from_numpy(rope[1]).to(dev))
     win = c.window if "swa" in c.kinds else 0
     ctl = P.pkv_setup_attn_control(d["seq_lens"], d["active"], d["bt_full"], d["bt_swa"],
                                    c.block, win, positions=d["positions"])
@@ -86,7 +89,7 @@ def gpu_step(wl, bufs, dev, use_layer_api=True, workspaces=None, k_packed=True):
     outs = []
     if use_layer_api and alternating(c):
         step = P.make_step(bufs, ctl, d["bt_full"], c.batch, c.hq, c.hkv, c.head_dim, c.block,
-                           c.window, wl.nb, k_packed=k_packed)
+                           c.window, wl.nb, k_packed=k_packed, rope_cos=rc, rope_sin=rs)
         for i in range(c.layers):
             out = torch.empty_like(d["q"][i])
             ws = ws_swa if i % 2 == 0 else ws_full
@@ -99,22 +102,24 @@ def gpu_step(wl, bufs, dev, use_layer_api=True, workspaces=None, k_packed=True):
             swa = kind == "swa"
             P.pkv_kv_cache_update(buf, d["k_new"][i], d["v_new"][i],
                                   ctl["upd_swa"] if swa else ctl["upd_full"], c.block, wl.nb,
-                                  wl.k_scale[i], wl.v_scale[i], k_packed=k_packed)
+                                  wl.k_scale[i], wl.v_scale[i], k_packed=k_packed,
+                                  rope_cos=rc, rope_sin=rs)
             if swa:
                 out = P.pkv_paged_decode_attn(d["q"][i], buf, ctl["bt_swa_trim"], ctl["pos_swa"],
                                               c.block, wl.nb, c.window, wl.k_scale[i],
                                               wl.v_scale[i], sm, c.hkv, workspace=ws_swa,
-                                              k_packed=k_packed)
+                                              k_packed=k_packed, rope_cos=rc, rope_sin=rs)
             else:
                 out = P.pkv_paged_decode_attn(d["q"][i], buf, d["bt_full"], ctl["pos_full"],
                                               c.block, wl.nb, 0, wl.k_scale[i], wl.v_scale[i],
-                                              sm, c.hkv, workspace=ws_full, k_packed=k_packed)
+                                              sm, c.hkv, workspace=ws_full, k_packed=k_packed,
+                                              rope_cos=rc, rope_sin=rs)
             outs.append(out)
     torch.cuda.synchronize()
     return outs, ctl
 
 
-def oracle_step(wl, snaps, layers=None, k_packed=True):
+def oracle_step(wl, snaps, layers=None, k_packed=True, rope=None):
     """snaps: list of host uint8 arrays (whole buffers, pre-step).  Updated in place."""
     c = wl.cfg
     half = wl.half_bytes
@@ -124,7 +129,9 @@ def oracle_step(wl, snaps, layers=None, k_packed=True):
     vn = [wl.v_new[i].float().numpy() for i in range(c.layers)]
     return OS.decode_step(bufs, q, kn, vn, wl.seq_lens, wl.active, wl.bt_full, wl.bt_swa,
                           c.block, c.hkv, c.window, wl.k_scale, wl.v_scale,
-                          1.0 / np.sqrt(c.head_dim), k_packed, layers=layers, kinds=list(c.kinds))
+                          1.0 / np.sqrt(c.head_dim), k_packed, layers=layers, kinds=list(c.kinds),
+                          rope_cos=None if rope is None else rope[0],
+                          rope_sin=None if rope is None else rope[1])
 
 
 def assert_close(got_bf16, ref, what=""):

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert P.pkv_abi_version() == 1
+    assert P.pkv_abi_version() == P.ABI_VERSION == 2
 
 
 @pytest.mark.parametrize("nb,H,Bk,D", [(36175, 1, 128, 64), (20880, 8, 32, 64), (7, 3, 16, 64)])
@@ -47,7 +47,7 @@ def test_trimmed_width_matches_oracle(Bk):
 def _attn(**over):
     a = dict(batch=2, q_heads=16, kv_heads=2, head_dim=64, block=32, num_blocks=10, window=0,
              q=None, k=None, k_packed=1, v=None, table=None, bt_stride=4, width=4, pos=None,
-             ks=0.125, vs=0.0625, sm=0.125, out=None, ws=None, ws_bytes=0, stream=None)
+             rc=None, rs=None, ks=0.125, vs=0.0625, sm=0.125, out=None, ws=None, ws_bytes=0, stream=None)
     a.update(over)
     return P.lib().pkv_paged_decode_attn(*a.values())
 
@@ -65,14 +65,28 @@ def test_attention_argument_errors():
     assert _attn(batch=0) == P.PKV_OK                      # empty batch is a no-op
 
 
+def test_rope_argument_errors():
+    """Rejected before any launch (the fake addresses are never dereferenced)."""
+    fake = dict(q=0x1000, k=0x1000, v=0x1000, table=0x1000, pos=0x1000, out=0x1000)
+    assert _attn(rc=0x2000, **fake) == P.PKV_ERR_ARG
+    assert b"rope" in P.lib().pkv_last_error()
+    assert _attn(rs=0x2000, **fake) == P.PKV_ERR_ARG
+    assert _attn(rc=0x2004, rs=0x2000, **fake) == P.PKV_ERR_ARG
+    assert b"aligned" in P.lib().pkv_last_error()
+    L = P.lib()
+    assert L.pkv_kv_cache_update(1, 1, 64, 16, 4, 0x1000, 0x1000, 0x1000, 1, 0x1000, 0x1000,
+                                 0x2000, None, 0.1, 0.1, None) == P.PKV_ERR_ARG
+    assert b"rope" in L.pkv_last_error()
+
+
 def test_update_and_setup_argument_errors():
     L = P.lib()
     assert L.pkv_kv_cache_update(1, 1, 32, 16, 4, None, None, None, 1, None, None,
-                                 0.1, 0.1, None) == P.PKV_ERR_UNSUPPORTED
+                                 None, None, 0.1, 0.1, None) == P.PKV_ERR_UNSUPPORTED
     assert L.pkv_kv_cache_update(1, 1, 64, 16, 4, None, None, None, 1, None, None,
-                                 0.1, 0.1, None) == P.PKV_ERR_ARG
+                                 None, None, 0.1, 0.1, None) == P.PKV_ERR_ARG
     assert L.pkv_kv_cache_update(0, 1, 64, 16, 4, None, None, None, 1, None, None,
-                                 0.1, 0.1, None) == P.PKV_OK
+                                 None, None, 0.1, 0.1, None) == P.PKV_OK
     assert L.pkv_setup_attn_control(1, 16, 128, None, None, None, None, 4, None, 4, 4, None,
                                     None, None, 9, None, None, None, None) == P.PKV_ERR_ARG
 
