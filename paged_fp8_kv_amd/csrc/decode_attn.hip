@@ -902,7 +902,10 @@ __global__ void __launch_bounds__(kThreads, kWGPerCU * kWavesPerWG / 4) decode_a
     s_pre[b] = n;
     longest = max(longest, n);
   }
-  atomicMax(&s_longest, longest);
+  // one LDS atomic per wave (64 lanes on one address would serialise)
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) longest = max(longest, __shfl_xor(longest, off));
+  if ((tid & 63) == 0) atomicMax(&s_longest, longest);
   __syncthreads();
   block_exclusive_scan(s_pre, B);
 
