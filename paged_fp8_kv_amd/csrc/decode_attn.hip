@@ -629,23 +629,51 @@ __device__ __forceinline__ void merge_item(const AttnArgs& a, int b, int h, int 
   }
 }
 
+// Exclusive prefix of the per-sequence sub-tile counts, pre(b) for
+// 0 <= b <= B (pre(B) = the total), held in LDS by the workgroup ...
+struct PreLds {
+  const int* s;
+  __device__ __forceinline__ int operator()(int i) const { return s[i]; }
+  // the last b in [0, B) with pre(b) * hkv <= x (uniform)
+  __device__ __forceinline__ int last_at_or_below(int B, int hkv, int64_t x) const {
+    int lo_i = 0, hi_i = B - 1;
+    while (lo_i < hi_i) {
+      const int mid = (lo_i + hi_i + 1) >> 1;
+      if (static_cast<int64_t>(s[mid]) * hkv <= x) lo_i = mid; else hi_i = mid - 1;
+    }
+    return __builtin_amdgcn_readfirstlane(lo_i);
+  }
+};
+
+// ... or, for B <= 64, in one register of every wave: lane b holds pre(b)
+// (lanes b >= B hold the total).
+struct PreReg {
+  int v;
+  int total;
+  __device__ __forceinline__ int operator()(int i) const {
+    return i < kWave ? __builtin_amdgcn_readlane(v, i) : total;
+  }
+  __device__ __forceinline__ int last_at_or_below(int B, int hkv, int64_t x) const {
+    // pre is non-decreasing, so the lanes that qualify are a prefix of [0, B)
+    const uint64_t m = __ballot(lane_id() < B && static_cast<int64_t>(v) * hkv <= x);
+    return __builtin_amdgcn_readfirstlane(__popcll(m) - 1);
+  }
+};
+
 // Offset (in the item line) of the first item that starts at or after x;
 // `total` when there is none.  Items are (b, h) in order, sequence b holding
-// Hkv items of s_pre[b+1]-s_pre[b] sub-tiles each.
-__device__ __forceinline__ int64_t first_item_start_at_or_after(const int* s_pre, int B, int hkv,
+// Hkv items of pre(b+1)-pre(b) sub-tiles each.
+template <class Pre>
+__device__ __forceinline__ int64_t first_item_start_at_or_after(const Pre& pre, int B, int hkv,
                                                                 int64_t x) {
-  const int64_t total = static_cast<int64_t>(s_pre[B]) * hkv;
+  const int64_t total = static_cast<int64_t>(pre(B)) * hkv;
   if (x >= total) return total;
-  int lo_i = 0, hi_i = B - 1;  // last b with s_pre[b] * hkv <= x
-  while (lo_i < hi_i) {
-    const int mid = (lo_i + hi_i + 1) >> 1;
-    if (static_cast<int64_t>(s_pre[mid]) * hkv <= x) lo_i = mid; else hi_i = mid - 1;
-  }
-  const int64_t base = static_cast<int64_t>(s_pre[lo_i]) * hkv;
-  const int n = s_pre[lo_i + 1] - s_pre[lo_i];
+  const int lo_i = pre.last_at_or_below(B, hkv, x);
+  const int64_t base = static_cast<int64_t>(pre(lo_i)) * hkv;
+  const int n = pre(lo_i + 1) - pre(lo_i);
   const int64_t h = (x - base + n - 1) / n;  // first item of b at or after x
   if (h < hkv) return base + h * n;
-  return static_cast<int64_t>(s_pre[lo_i + 1]) * hkv;  // first item of the next sequence with work
+  return static_cast<int64_t>(pre(lo_i + 1)) * hkv;  // first item of the next sequence with work
 }
 
 // Half-split rotation of the lane's 16 query dims (16q .. 16q+15, packed bf16
@@ -678,32 +706,23 @@ __device__ __forceinline__ void rotate_queries(u32x4_t& q0, u32x4_t& q1, const f
 // schedule.  Items that lie wholly inside are written out; pieces of items
 // cut by chunk boundaries go through partial slots 2*cid / 2*cid+1 and are
 // merged by the last piece to arrive.
-template <int BK, bool WINDOWED, bool KP, bool ROPE>
-__device__ __forceinline__ void process_chunk(const AttnArgs& a, const int* s_pre, int B, int cid,
+template <int BK, bool WINDOWED, bool KP, bool ROPE, class Pre>
+__device__ __forceinline__ void process_chunk(const AttnArgs& a, const Pre& s_pre, int B, int cid,
                                               const Sched sc, int64_t cur, int64_t wend,
                                               uint8_t* ring) {
   const int lane = lane_id();
   const int m = lane & 15, q = lane >> 4, e = m >> 3, g = m & 7;
   const int64_t wbeg = cur;
-  // locate the first item: the last b with s_pre[b] * Hkv <= cur (uniform)
-  int b;
-  {
-    int lo_i = 0, hi_i = B - 1;
-    while (lo_i < hi_i) {
-      const int mid = (lo_i + hi_i + 1) >> 1;
-      if (static_cast<int64_t>(s_pre[mid]) * a.Hkv <= cur) lo_i = mid; else hi_i = mid - 1;
-    }
-    b = lo_i;
-  }
-  b = __builtin_amdgcn_readfirstlane(b);
-  int n = s_pre[b + 1] - s_pre[b];
-  int64_t rel = cur - static_cast<int64_t>(s_pre[b]) * a.Hkv;
+  // locate the first item: the last b with pre(b) * Hkv <= cur (uniform)
+  int b = s_pre.last_at_or_below(B, a.Hkv, cur);
+  int n = s_pre(b + 1) - s_pre(b);
+  int64_t rel = cur - static_cast<int64_t>(s_pre(b)) * a.Hkv;
   int h = __builtin_amdgcn_readfirstlane(static_cast<int>(rel / n));
   int j = __builtin_amdgcn_readfirstlane(static_cast<int>(rel % n));
 
   while (cur < wend && b < B) {
-    n = __builtin_amdgcn_readfirstlane(s_pre[b + 1] - s_pre[b]);
-    const int pre_b = __builtin_amdgcn_readfirstlane(s_pre[b]);
+    n = __builtin_amdgcn_readfirstlane(s_pre(b + 1) - s_pre(b));
+    const int pre_b = __builtin_amdgcn_readfirstlane(s_pre(b));
     const int seg = static_cast<int>(min(static_cast<int64_t>(n - j), wend - cur));
     const int64_t item_beg = static_cast<int64_t>(pre_b) * a.Hkv + static_cast<int64_t>(h) * n;
     const int64_t item_end = item_beg + n;
@@ -878,40 +897,21 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const int* s_pr
       h = 0;
       do {
         ++b;
-      } while (b < B && s_pre[b + 1] == s_pre[b]);
+      } while (b < B && s_pre(b + 1) == s_pre(b));
       b = __builtin_amdgcn_readfirstlane(b);
     }
   }
 }
 
-template <int BK, bool WINDOWED, bool KP, bool ROPE>
-__global__ void __launch_bounds__(kThreads, kWGPerCU * kWavesPerWG / 4) decode_attn_kernel(AttnArgs a) {
-  extern __shared__ int s_pre[];  // [B + 1] prefix of per-sequence sub-tile counts
-  __shared__ int s_longest;       // longest item, in sub-tiles
-  __shared__ __attribute__((aligned(16))) uint8_t s_ring[kWavesPerWG * kDepth * kSlotBytes];
-  uint8_t* ring = s_ring + (threadIdx.x >> 6) * (kDepth * kSlotBytes);
+// Everything after the prefix: rows without work, the static split of the
+// item line over the W waves, and the wave's share.
+template <int BK, bool WINDOWED, bool KP, bool ROPE, class Pre>
+__device__ __forceinline__ void run_shares(const AttnArgs& a, const Pre& pre, int B, int longest,
+                                           uint8_t* ring) {
   const int tid = threadIdx.x;
-  const int B = a.B;
-  if (tid == 0) s_longest = 0;
-  __syncthreads();
-  int longest = 0;
-  for (int b = tid; b < B; b += kThreads) {
-    int lo = 0;
-    bool inv;
-    const int n = seq_subtiles<BK, WINDOWED>(a, a.frame_pos[b], &lo, &inv);
-    s_pre[b] = n;
-    longest = max(longest, n);
-  }
-  // one LDS atomic per wave (64 lanes on one address would serialise)
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) longest = max(longest, __shfl_xor(longest, off));
-  if ((tid & 63) == 0) atomicMax(&s_longest, longest);
-  __syncthreads();
-  block_exclusive_scan(s_pre, B);
-
   // rows with no work: +0 for inactive sequences, NaN for invalid positions
   for (int b = blockIdx.x; b < B; b += gridDim.x) {
-    if (s_pre[b + 1] != s_pre[b]) continue;
+    if (pre(b + 1) != pre(b)) continue;
     int lo = 0;
     bool inv;
     seq_subtiles<BK, WINDOWED>(a, a.frame_pos[b], &lo, &inv);
@@ -926,7 +926,7 @@ __global__ void __launch_bounds__(kThreads, kWGPerCU * kWavesPerWG / 4) decode_a
   // item is tiny or at most half a share, wave w takes the whole items whose
   // first sub-tile falls in its share (no partials, no merge); otherwise
   // shares are exact and cut items are merged through the workspace.
-  const int64_t total = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(s_pre[B])) * a.Hkv;
+  const int64_t total = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(pre(B))) * a.Hkv;
   if (total == 0) return;
   const int W = a.n_workers;
   const int wid = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerWG + (tid >> 6));
@@ -934,13 +934,63 @@ __global__ void __launch_bounds__(kThreads, kWGPerCU * kWavesPerWG / 4) decode_a
   const int64_t cb = static_cast<int64_t>(wid) * per;
   if (cb >= total) return;
   const Sched sc{per};
-  const int longest_item = __builtin_amdgcn_readfirstlane(s_longest);
-  if (longest_item <= kTinyItem || 2 * static_cast<int64_t>(longest_item) <= per) {
-    const int64_t lo_w = first_item_start_at_or_after(s_pre, B, a.Hkv, cb);
-    const int64_t hi_w = first_item_start_at_or_after(s_pre, B, a.Hkv, min(cb + per, total));
-    if (lo_w < hi_w) process_chunk<BK, WINDOWED, KP, ROPE>(a, s_pre, B, wid, sc, lo_w, hi_w, ring);
+  if (longest <= kTinyItem || 2 * static_cast<int64_t>(longest) <= per) {
+    const int64_t lo_w = first_item_start_at_or_after(pre, B, a.Hkv, cb);
+    const int64_t hi_w = first_item_start_at_or_after(pre, B, a.Hkv, min(cb + per, total));
+    if (lo_w < hi_w) process_chunk<BK, WINDOWED, KP, ROPE>(a, pre, B, wid, sc, lo_w, hi_w, ring);
   } else {
-    process_chunk<BK, WINDOWED, KP, ROPE>(a, s_pre, B, wid, sc, cb, min(cb + per, total), ring);
+    process_chunk<BK, WINDOWED, KP, ROPE>(a, pre, B, wid, sc, cb, min(cb + per, total), ring);
+  }
+}
+
+template <int BK, bool WINDOWED, bool KP, bool ROPE>
+__global__ void __launch_bounds__(kThreads, kWGPerCU * kWavesPerWG / 4) decode_attn_kernel(AttnArgs a) {
+  extern __shared__ int s_pre[];  // [B + 1] prefix of per-sequence sub-tile counts
+  __shared__ int s_longest;       // longest item, in sub-tiles
+  __shared__ __attribute__((aligned(16))) uint8_t s_ring[kWavesPerWG * kDepth * kSlotBytes];
+  uint8_t* ring = s_ring + (threadIdx.x >> 6) * (kDepth * kSlotBytes);
+  const int tid = threadIdx.x;
+  const int B = a.B;
+  if (B <= kWave) {
+    // Every wave scans the (at most 64) positions in registers: no LDS, no
+    // barrier between the position load and the wave's first item.
+    const int lane = tid & (kWave - 1);
+    int n = 0;
+    if (lane < B) {
+      int lo = 0;
+      bool inv;
+      n = seq_subtiles<BK, WINDOWED>(a, a.frame_pos[lane], &lo, &inv);
+    }
+    int x = n;  // inclusive prefix over the lanes
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int y = __shfl_up(x, off, kWave);
+      if (lane >= off) x += y;
+    }
+    int longest = n;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) longest = max(longest, __shfl_xor(longest, off));
+    const PreReg pre{x - n, __builtin_amdgcn_readlane(x, kWave - 1)};
+    run_shares<BK, WINDOWED, KP, ROPE>(a, pre, B, __builtin_amdgcn_readfirstlane(longest), ring);
+  } else {
+    if (tid == 0) s_longest = 0;
+    __syncthreads();
+    int longest = 0;
+    for (int b = tid; b < B; b += kThreads) {
+      int lo = 0;
+      bool inv;
+      const int n = seq_subtiles<BK, WINDOWED>(a, a.frame_pos[b], &lo, &inv);
+      s_pre[b] = n;
+      longest = max(longest, n);
+    }
+    // one LDS atomic per wave (64 lanes on one address would serialise)
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) longest = max(longest, __shfl_xor(longest, off));
+    if ((tid & 63) == 0) atomicMax(&s_longest, longest);
+    __syncthreads();
+    block_exclusive_scan(s_pre, B);
+    run_shares<BK, WINDOWED, KP, ROPE>(a, PreLds{s_pre}, B,
+                                       __builtin_amdgcn_readfirstlane(s_longest), ring);
   }
   wait_vmcnt<0>();  // no direct-to-LDS load outlives the wave
 }
