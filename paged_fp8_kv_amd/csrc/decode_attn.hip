@@ -211,12 +211,21 @@ __device__ __forceinline__ i32x4_t tile_desc(const uint8_t* p, int bytes) {
 // direct-to-LDS load before each LDS read.  Completion is tracked by the
 // explicit vmcnt waits below; the compiler's own waits for other loads only
 // become stricter.
+// NT marks the load non-temporal: the K/V bytes are read exactly once, and
+// full-attention layers stream their whole context through the caches.
+template <bool NT>
 __device__ __forceinline__ void dma16(i32x4_t desc, uint32_t voff, uint32_t soff,
                                       uint32_t lds_addr) {
-  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
-               :
-               : "v"(voff), "s"(desc), "s"(soff), "{m0}"(lds_addr)
-               : "memory");
+  if constexpr (NT)
+    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen nt lds"
+                 :
+                 : "v"(voff), "s"(desc), "s"(soff), "{m0}"(lds_addr)
+                 : "memory");
+  else
+    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :
+                 : "v"(voff), "s"(desc), "s"(soff), "{m0}"(lds_addr)
+                 : "memory");
 }
 __device__ __forceinline__ uint32_t lds_addr_of(const uint8_t* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)(const_cast<uint8_t*>(p))));
@@ -255,6 +264,9 @@ __device__ __forceinline__ void wait_vmcnt_slots(int n) {
 
 template <int BK, bool WINDOWED, bool KP>
 struct Item {
+  // non-temporal K/V loads for full attention (measured: faster there, and
+  // no gain for the short window reads)
+  static constexpr bool kStreamNT = !WINDOWED;
   const uint8_t* kbase;
   const uint8_t* vbase;
   uint8_t* kw;          // writable halves, for the fused new-token write
@@ -338,13 +350,13 @@ struct Item {
                                                         (((lane & 7) ^ (lane >> 3) ^ j) * 16))
                                 : static_cast<uint32_t>(v_row_token(16 * j + (lane >> 2)) * kHeadDim +
                                                         (lane & 3) * 16);
-        dma16(rk, kof, so, dst + 1024 * j);
+        dma16<kStreamNT>(rk, kof, so, dst + 1024 * j);
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int t = v_row_token(16 * j + (lane >> 2));
         const uint32_t vof = static_cast<uint32_t>(t * kHeadDim + (lane & 3) * 16);
-        dma16(rv, vof, so, dst + 2048 + 1024 * j);
+        dma16<kStreamNT>(rv, vof, so, dst + 2048 + 1024 * j);
       }
     } else {
       // BK == 16: each load instruction covers one of the two blocks of the
@@ -358,9 +370,9 @@ struct Item {
         const int t = v_row_token(16 * j + (lane >> 2)) - 16 * j;
         const uint32_t kof = KP ? static_cast<uint32_t>((lane >> 3) * 128 + (((lane & 7) ^ (lane >> 3) ^ j) * 16))
                                 : static_cast<uint32_t>(t * kHeadDim + (lane & 3) * 16);
-        dma16(rk, kof, 0u, dst + 1024 * j);
+        dma16<kStreamNT>(rk, kof, 0u, dst + 1024 * j);
         const uint32_t vof = static_cast<uint32_t>(t * kHeadDim + (lane & 3) * 16);
-        dma16(rv, vof, 0u, dst + 2048 + 1024 * j);
+        dma16<kStreamNT>(rv, vof, 0u, dst + 2048 + 1024 * j);
       }
     }
   }
