@@ -329,7 +329,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": f"decode_attn_kernel<{cfg.block}, false> (full layers)",
+                     "kernel": f"decode_attn_kernel<{cfg.block}, false, {str(args.k_layout == 'packed').lower()}, {str(args.rope).lower()}> (full layers)",
                      "bytes_per_launch": full_bytes, "avg_launch_us": round(full_us, 2),
                      "swa_avg_launch_us": round(swa_us, 2) if swa_us else None},
         "cpu_baseline": None,
