@@ -583,13 +583,60 @@ __device__ __forceinline__ void write_partial(const AttnArgs& a, int slot, const
   }
 }
 
-// Combine the P pieces of item (b, h) -- chunk cf's tail slot, then the head
-// slots of chunks cf+1 .. cf+P-1 -- and write the output row.  Eight pieces
-// are fetched per round trip; lane (g = lane & 7, part = lane >> 3) owns
-// dims 8*part .. 8*part+7 of head g.  Rounds combine with a running maximum.
-__device__ __forceinline__ void merge_item(const AttnArgs& a, int b, int h, int cf, int P, int lane) {
+// Write one piece's partial into workgroup LDS, same layout as a workspace slot.
+__device__ __forceinline__ void write_partial_lds(float* dst, const float (&o)[16], float mx,
+                                                  float lsum, int lane) {
+  const int m = lane & 15, q = lane >> 4;
+  if (m < 8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<f32x4_t*>(dst + m * kHeadDim + 16 * q + 4 * i) =
+          f32x4_t{o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
+    if (q == 0) {
+      dst[8 * kHeadDim + m] = mx;
+      dst[8 * kHeadDim + 8 + m] = lsum;
+    }
+  }
+}
+
+// Pieces of an item in workspace slots: chunk cf's tail slot, then the head
+// slots of chunks cf+1 .. (device-coherent loads).
+struct SlotPieces {
+  __amdgpu_buffer_rsrc_t r;
+  int cf;
+  __device__ __forceinline__ void load(int k, int g, int part, float& m, float& l, u32x4_t& o0,
+                                       u32x4_t& o1) const {
+    const int sl = (k == 0) ? 2 * cf + 1 : 2 * (cf + k);
+    const int base = sl * kSlotBytesF;
+    m = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, base + (8 * kHeadDim + g) * 4, 0, kCoherent));
+    l = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, base + (8 * kHeadDim + 8 + g) * 4, 0, kCoherent));
+    o0 = __builtin_amdgcn_raw_buffer_load_b128(r, base + (g * kHeadDim + 8 * part) * 4, 0, kCoherent);
+    o1 = __builtin_amdgcn_raw_buffer_load_b128(r, base + (g * kHeadDim + 8 * part + 4) * 4, 0, kCoherent);
+  }
+};
+
+// The two pieces of an item cut once inside one workgroup, in LDS.
+struct LdsPieces {
+  const float* p0;
+  const float* p1;
+  __device__ __forceinline__ void load(int k, int g, int part, float& m, float& l, u32x4_t& o0,
+                                       u32x4_t& o1) const {
+    const float* p = k == 0 ? p0 : p1;
+    m = p[8 * kHeadDim + g];
+    l = p[8 * kHeadDim + 8 + g];
+    o0 = *reinterpret_cast<const u32x4_t*>(p + g * kHeadDim + 8 * part);
+    o1 = *reinterpret_cast<const u32x4_t*>(p + g * kHeadDim + 8 * part + 4);
+  }
+};
+
+// Combine the P pieces of item (b, h), in piece order, and write the output
+// row.  Eight pieces are fetched per round; lane (g = lane & 7, part =
+// lane >> 3) owns dims 8*part .. 8*part+7 of head g.  Rounds combine with a
+// running maximum.
+template <class Src>
+__device__ __forceinline__ void merge_item(const AttnArgs& a, int b, int h, int P, int lane,
+                                           const Src& src) {
   const int g = lane & 7, part = lane >> 3;
-  const __amdgpu_buffer_rsrc_t r = partial_rsrc(a);
   float mrun = -INFINITY, lrun = 0.f;
   float acc[8];
 #pragma unroll
@@ -598,15 +645,7 @@ __device__ __forceinline__ void merge_item(const AttnArgs& a, int b, int h, int 
     float mk[8], lk[8];
     u32x4_t o0[8], o1[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int k = min(k0 + i, P - 1);
-      const int sl = (k == 0) ? 2 * cf + 1 : 2 * (cf + k);
-      const int base = sl * kSlotBytesF;
-      mk[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, base + (8 * kHeadDim + g) * 4, 0, kCoherent));
-      lk[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, base + (8 * kHeadDim + 8 + g) * 4, 0, kCoherent));
-      o0[i] = __builtin_amdgcn_raw_buffer_load_b128(r, base + (g * kHeadDim + 8 * part) * 4, 0, kCoherent);
-      o1[i] = __builtin_amdgcn_raw_buffer_load_b128(r, base + (g * kHeadDim + 8 * part + 4) * 4, 0, kCoherent);
-    }
+    for (int i = 0; i < 8; ++i) src.load(min(k0 + i, P - 1), g, part, mk[i], lk[i], o0[i], o1[i]);
     float mx = mrun;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -714,6 +753,14 @@ __device__ __forceinline__ void rotate_queries(u32x4_t& q0, u32x4_t& q1, const f
   q1 = u32x4_t{r[4], r[5], r[6], r[7]};
 }
 
+// Workgroup LDS for partials of items cut once inside the workgroup: two
+// piece slots per wave (head piece, tail piece) and one arrival counter per
+// chunk of the workgroup.
+struct WgLocal {
+  float* part;  // [kWavesPerWG][2][kSlotFloats]
+  int* cnt;     // [kWavesPerWG]
+};
+
 // Process the sub-tiles [cur, wend) of the item line, chunk `cid` of the
 // schedule.  Items that lie wholly inside are written out; pieces of items
 // cut by chunk boundaries go through partial slots 2*cid / 2*cid+1 and are
@@ -721,7 +768,7 @@ __device__ __forceinline__ void rotate_queries(u32x4_t& q0, u32x4_t& q1, const f
 template <int BK, bool WINDOWED, bool KP, bool ROPE, class Pre>
 __device__ __forceinline__ void process_chunk(const AttnArgs& a, const Pre& s_pre, int B, int cid,
                                               const Sched sc, int64_t cur, int64_t wend,
-                                              uint8_t* ring) {
+                                              uint8_t* ring, const WgLocal wg) {
   const int lane = lane_id();
   const int m = lane & 15, q = lane >> 4, e = m >> 3, g = m & 7;
   const int64_t wbeg = cur;
@@ -886,6 +933,25 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const Pre& s_pr
         for (int i = 0; i < 16; ++i) o[i] *= f;
         store_bf16x16(a.out + (static_cast<int64_t>(b) * a.Hq + h * a.G + g) * kHeadDim + 16 * q, o);
       }
+    } else if (sc.of(item_end - 1) == sc.of(item_beg) + 1 &&
+               sc.of(item_beg) / kWavesPerWG == sc.of(item_end - 1) / kWavesPerWG) {
+      // cut once, both pieces in this workgroup: hand off through LDS
+      const int cf = sc.of(item_beg), cl = cf + 1;
+      const int slot = (item_beg >= wbeg) ? 1 : 0;
+      write_partial_lds(wg.part + (2 * (cid % kWavesPerWG) + slot) * kSlotFloats, o, s.m,
+                        bad ? NAN : lsum, lane);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      int old = 0;
+      if (lane == 0)
+        old = __hip_atomic_fetch_add(wg.cnt + cf % kWavesPerWG, 1, __ATOMIC_ACQ_REL,
+                                     __HIP_MEMORY_SCOPE_WORKGROUP);
+      old = __builtin_amdgcn_readfirstlane(__shfl(old, 0, 64));
+      if (old == 1) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        merge_item(a, b, h, 2, lane,
+                   LdsPieces{wg.part + (2 * (cf % kWavesPerWG) + 1) * kSlotFloats,
+                             wg.part + (2 * (cl % kWavesPerWG) + 0) * kSlotFloats});
+      }
     } else {
       const int cf = sc.of(item_beg), cl = sc.of(item_end - 1);
       const int slot = (item_beg >= wbeg) ? 2 * cid + 1 : 2 * cid;
@@ -898,7 +964,7 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const Pre& s_pr
       const int ncontrib = cl - cf + 1;
       if (old == ncontrib - 1) {
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        merge_item(a, b, h, cf, ncontrib, lane);
+        merge_item(a, b, h, ncontrib, lane, SlotPieces{partial_rsrc(a), cf});
         if (lane == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
@@ -919,7 +985,7 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const Pre& s_pr
 // item line over the W waves, and the wave's share.
 template <int BK, bool WINDOWED, bool KP, bool ROPE, class Pre>
 __device__ __forceinline__ void run_shares(const AttnArgs& a, const Pre& pre, int B, int longest,
-                                           uint8_t* ring) {
+                                           uint8_t* ring, const WgLocal wg) {
   const int tid = threadIdx.x;
   // rows with no work: +0 for inactive sequences, NaN for invalid positions
   for (int b = blockIdx.x; b < B; b += gridDim.x) {
@@ -944,14 +1010,21 @@ __device__ __forceinline__ void run_shares(const AttnArgs& a, const Pre& pre, in
   const int wid = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerWG + (tid >> 6));
   const int64_t per = (total + W - 1) / W;
   const int64_t cb = static_cast<int64_t>(wid) * per;
+  const bool whole_items = longest <= kTinyItem || 2 * static_cast<int64_t>(longest) <= per;
+  if (!whole_items) {
+    // items may be cut: clear the workgroup's LDS arrival counters (every
+    // wave of the workgroup gets here; the decision is the same for all)
+    if (tid < kWavesPerWG) wg.cnt[tid] = 0;
+    __syncthreads();
+  }
   if (cb >= total) return;
   const Sched sc{per};
-  if (longest <= kTinyItem || 2 * static_cast<int64_t>(longest) <= per) {
+  if (whole_items) {
     const int64_t lo_w = first_item_start_at_or_after(pre, B, a.Hkv, cb);
     const int64_t hi_w = first_item_start_at_or_after(pre, B, a.Hkv, min(cb + per, total));
-    if (lo_w < hi_w) process_chunk<BK, WINDOWED, KP, ROPE>(a, pre, B, wid, sc, lo_w, hi_w, ring);
+    if (lo_w < hi_w) process_chunk<BK, WINDOWED, KP, ROPE>(a, pre, B, wid, sc, lo_w, hi_w, ring, wg);
   } else {
-    process_chunk<BK, WINDOWED, KP, ROPE>(a, pre, B, wid, sc, cb, min(cb + per, total), ring);
+    process_chunk<BK, WINDOWED, KP, ROPE>(a, pre, B, wid, sc, cb, min(cb + per, total), ring, wg);
   }
 }
 
@@ -960,9 +1033,12 @@ __global__ void __launch_bounds__(kThreads, kWGPerCU * kWavesPerWG / 4) decode_a
   extern __shared__ int s_pre[];  // [B + 1] prefix of per-sequence sub-tile counts
   __shared__ int s_longest;       // longest item, in sub-tiles
   __shared__ __attribute__((aligned(16))) uint8_t s_ring[kWavesPerWG * kDepth * kSlotBytes];
+  __shared__ __attribute__((aligned(16))) float s_part[kWavesPerWG * 2 * kSlotFloats];
+  __shared__ int s_cnt[kWavesPerWG];
   uint8_t* ring = s_ring + (threadIdx.x >> 6) * (kDepth * kSlotBytes);
   const int tid = threadIdx.x;
   const int B = a.B;
+  const WgLocal wg{s_part, s_cnt};
   if (B <= kWave) {
     // Every wave scans the (at most 64) positions in registers: no LDS, no
     // barrier between the position load and the wave's first item.
@@ -983,7 +1059,7 @@ __global__ void __launch_bounds__(kThreads, kWGPerCU * kWavesPerWG / 4) decode_a
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) longest = max(longest, __shfl_xor(longest, off));
     const PreReg pre{x - n, __builtin_amdgcn_readlane(x, kWave - 1)};
-    run_shares<BK, WINDOWED, KP, ROPE>(a, pre, B, __builtin_amdgcn_readfirstlane(longest), ring);
+    run_shares<BK, WINDOWED, KP, ROPE>(a, pre, B, __builtin_amdgcn_readfirstlane(longest), ring, wg);
   } else {
     if (tid == 0) s_longest = 0;
     __syncthreads();
@@ -1002,7 +1078,7 @@ __global__ void __launch_bounds__(kThreads, kWGPerCU * kWavesPerWG / 4) decode_a
     __syncthreads();
     block_exclusive_scan(s_pre, B);
     run_shares<BK, WINDOWED, KP, ROPE>(a, PreLds{s_pre}, B,
-                                       __builtin_amdgcn_readfirstlane(s_longest), ring);
+                                       __builtin_amdgcn_readfirstlane(s_longest), ring, wg);
   }
   wait_vmcnt<0>();  // no direct-to-LDS load outlives the wave
 }
