@@ -104,11 +104,33 @@ def cpu_baseline(wl, bufs_dev, seconds):
                       f"({done_bytes / 1e6:.1f} MB of KV) in {dt:.1f} s, numpy float64, 1 thread"}
 
 
+def identity_tables(wl):
+    """The control run's tables: sequence b's full-table blocks are the pool's
+    ids b*W .. b*W + n - 1 (W = table width) and its window blocks follow all
+    of those, so every sequence streams one contiguous region."""
+    import dataclasses
+    c = wl.cfg
+    B, Wd = c.batch, wl.bt_full.shape[1]
+    full = np.full_like(wl.bt_full, -1)
+    swa = np.full_like(wl.bt_swa, -1)
+    keep = int((wl.bt_swa >= 0).sum(axis=1).max()) if (wl.bt_swa >= 0).any() else 0
+    if B * (Wd + keep) > wl.nb:
+        raise SystemExit(f"identity tables need {B * (Wd + keep)} blocks, the pool has {wl.nb}")
+    for b in range(B):
+        n = int((wl.bt_full[b] >= 0).sum())
+        full[b, :n] = b * Wd + np.arange(n)
+        cols = np.nonzero(wl.bt_swa[b] >= 0)[0]
+        swa[b, cols] = B * Wd + b * keep + np.arange(len(cols))
+    ref = np.unique(np.concatenate([full[full >= 0], swa[swa >= 0]])).astype(np.int64)
+    return dataclasses.replace(wl, bt_full=full.astype(np.int32), bt_swa=swa.astype(np.int32),
+                               referenced=ref)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="cfg3")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -120,6 +142,12 @@ def main():
                     help="K half arrangement: packed token pairs (default) or token-major rows")
     ap.add_argument("--rope", action="store_true",
                     help="turn the queries and new keys by per-sequence rotary cos/sin")
+    ap.add_argument("--control", choices=["random", "identity"], default="random",
+                    help="identity: every sequence's blocks consecutive in the pool (isolates "
+                         "the cost of the gather)")
+    ap.add_argument("--cold-steps", type=int, default=10,
+                    help="steps timed one by one after overwriting 1 GiB (flushes the "
+                         "256 MB Infinity Cache); 0 = none")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -139,6 +167,8 @@ def main():
     cfg = W.CONFIGS[args.config]
     hbm = torch.cuda.mem_get_info(dev)[1]
     wl = W.make_workload(cfg, hbm_bytes=hbm)
+    if args.control == "identity":
+        wl = identity_tables(wl)
     log(f"workload {cfg.name}: nb={wl.nb}, {cfg.n_buffers} buffers of "
         f"{2 * wl.half_bytes / 1e9:.2f} GB")
     bufs = []
@@ -258,14 +288,33 @@ def main():
             g.replay() if use_graph else step()
         torch.cuda.synchronize()
 
-    # ---- timed region: whole steps
+    # ---- timed region: whole steps (an event before each step for percentiles)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for k in range(args.steps):
+        marks[k].record()
         g.replay() if use_graph else step()
+    marks[-1].record()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     ms = dt * 1e3 / args.steps
+    per_step = np.array([marks[k].elapsed_time(marks[k + 1]) for k in range(args.steps)])
+
+    # ---- cold steps: each after overwriting 1 GiB, which evicts the Infinity Cache
+    cold = []
+    if args.cold_steps > 0:
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        for k in range(args.cold_steps):
+            scratch.fill_(k & 0xff)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay() if use_graph else step()
+            b.record()
+            torch.cuda.synchronize()
+            cold.append(a.elapsed_time(b))
+        del scratch
 
     # ---- dominant kernel: the full-layer launches of a step, made exactly as the
     # step makes them but back to back between two events on their stream (the
@@ -302,7 +351,8 @@ def main():
     if os.path.exists(TRAFFIC_FILE):
         tr = json.load(open(TRAFFIC_FILE))
         if (tr.get("kernel_sha") == kernel_sha() and tr.get("config") == args.config
-                and args.k_layout == "packed" and args.tables == "padded" and not args.rope):
+                and args.k_layout == "packed" and args.tables == "padded" and not args.rope
+                and args.control == "random"):
             traffic = tr.get("bytes_per_launch")
     value = step_bytes / (ms * 1e-3) / 1e9
     result = {
@@ -322,8 +372,10 @@ def main():
                    "q_heads": cfg.hq, "kv_heads": cfg.hkv, "head_dim": cfg.head_dim,
                    "block": cfg.block, "context": "8192" if cfg.ctx[0] == "fixed" else str(cfg.ctx),
                    "window": cfg.window, "num_blocks": wl.nb, "k_layout": args.k_layout, "tables": args.tables,
-                   "rope": args.rope, "graph": use_graph},
+                   "rope": args.rope, "control": args.control, "graph": use_graph},
         "tokens_per_s": round(cfg.batch / (ms * 1e-3), 1),
+        "step_ms_p10_p50_p90": [round(float(np.percentile(per_step, p)), 4) for p in (10, 50, 90)],
+        "cold_step_ms_median": round(float(np.median(cold)), 4) if cold else None,
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
         "kv_bytes_per_step": step_bytes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
