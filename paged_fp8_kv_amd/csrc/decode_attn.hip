@@ -51,6 +51,13 @@ constexpr float kRescaleSlack = 8.0f; // log2 units
 #endif
 constexpr int kDepth = PKV_DEPTH;     // sub-tiles in flight per wave
 constexpr int kTinyItem = 8;          // items this short (sub-tiles) are never split
+// Fixed cost of starting a short item (shorter than a share), in sub-tiles:
+// the wait for its set-up loads and first K/V loads plus the fill and drain
+// of the ring (about 2.4 us, measured, against 0.6 us per streamed sub-tile).
+// The static split of full-attention launches counts it on top of the
+// item's sub-tiles so that waves given many short items are not the last to
+// finish (window items are all short and alike: they are not weighted).
+constexpr int kItemCost = 4;
 // Waves per SIMD the kernel is compiled for (= workgroups per CU, 4 waves
 // each); the stream-K shares assume every worker is resident at once.
 #ifndef PKV_WG_PER_CU
@@ -768,7 +775,7 @@ struct WgLocal {
 template <int BK, bool WINDOWED, bool KP, bool ROPE, class Pre>
 __device__ __forceinline__ void process_chunk(const AttnArgs& a, const Pre& s_pre, int B, int cid,
                                               const Sched sc, int64_t cur, int64_t wend,
-                                              uint8_t* ring, const WgLocal wg) {
+                                              uint8_t* ring, const WgLocal wg, int64_t per_r) {
   const int lane = lane_id();
   const int m = lane & 15, q = lane >> 4, e = m >> 3, g = m & 7;
   const int64_t wbeg = cur;
@@ -790,7 +797,9 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const Pre& s_pr
     // sub-tile (j) and its table window do not depend on the position.
     const int fp_raw = a.frame_pos[b];
     Item<BK, WINDOWED, KP> it(a, b, h);
-    if (!WINDOWED) it.load_window((j * kSub) / BK);
+    // without a window: the window must hold column jr*kSub/BK; only an item
+    // shorter than a share can carry a start cost (jr = j - kItemCost)
+    if (!WINDOWED) it.load_window(((n < per_r + kItemCost ? max(j - kItemCost, 0) : j) * kSub) / BK);
     u32x4_t q0 = {0u, 0u, 0u, 0u}, q1 = {0u, 0u, 0u, 0u};
     if (g < a.G) {
       const uint16_t* qp = a.q + (static_cast<int64_t>(b) * a.Hq + h * a.G + g) * kHeadDim + 16 * q;
@@ -825,7 +834,26 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const Pre& s_pr
     const int hi = __builtin_amdgcn_readfirstlane(fp_raw);
     const int lo = WINDOWED ? max(0, hi - a.window + 1) : 0;
     it.set_range(lo, hi);
-    if (WINDOWED) it.load_window(it.clampc(((lo / kSub + j) * kSub) / BK));
+    // On the line the item holds its start cost c0 (0 or kItemCost) first,
+    // then its sub-tiles: this piece's sub-tiles are [jr, jr + segr).
+    const int c0 = n - (hi / kSub - lo / kSub + 1);
+    const int jr = max(j - c0, 0);
+    const int segr = max(0, j + seg - c0 - jr);
+    const int64_t real_beg = item_beg + c0;  // where the item's sub-tiles start on the line
+    if (segr == 0) {
+      // the piece covers only the start cost: no keys, no partial
+      cur += seg;
+      j = 0;
+      if (++h == a.Hkv) {
+        h = 0;
+        do {
+          ++b;
+        } while (b < B && s_pre(b + 1) == s_pre(b));
+        b = __builtin_amdgcn_readfirstlane(b);
+      }
+      continue;
+    }
+    if (WINDOWED) it.load_window(it.clampc(((lo / kSub + jr) * kSub) / BK));
 
     if (rope) rotate_queries(q0, q1, rc, rs, q >= 2);
     // expanded queries: qx[i][k] holds q[g][16q + 4i + k] in the half of parity e
@@ -846,8 +874,8 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const Pre& s_pr
     // write, the segment holding it quantises the token's K/V (lane j: dim j),
     // patches them into that sub-tile's slot before it is read, and stores
     // them into the cache slot of position hi.
-    const int t_new = (a.k_new != nullptr && hi / kSub >= lo / kSub + j &&
-                       hi / kSub < lo / kSub + j + seg) ? hi / kSub : -1;
+    const int t_new = (a.k_new != nullptr && hi / kSub >= lo / kSub + jr &&
+                       hi / kSub < lo / kSub + jr + segr) ? hi / kSub : -1;
     uint32_t kcode = 0, vcode = 0;
     if (t_new >= 0) {
       float kf = bf16_bits_to_f32(kn_bits);
@@ -862,8 +890,8 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const Pre& s_pr
     for (int t = 0; t < 4; ++t) s.acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     s.m = -INFINITY;
     s.l = 0.f;
-    const int t0 = lo / kSub + j;
-    const int tlast = t0 + seg - 1;
+    const int t0 = lo / kSub + jr;
+    const int tlast = t0 + segr - 1;
 
     // Two-stage software pipeline over the segment's sub-tiles, run per
     // window of kWinEntries table entries.
@@ -873,8 +901,9 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const Pre& s_pr
     int span = __builtin_amdgcn_readfirstlane(kWinEntries - 16 * ((threadIdx.x >> 6) & 3));
     for (int tw = t0; tw <= tlast;) {
       const int cw0 = it.clampc((tw * kSub) / BK);
-      if (cw0 != it.tab_base) it.load_window(cw0);
-      const int twl = max(tw, min(tlast, ((cw0 + span) * BK) / kSub - 1));
+      if (cw0 < it.tab_base || cw0 >= it.tab_base + kWinEntries) it.load_window(cw0);
+      const int cend = min(it.tab_base + kWinEntries, cw0 + span);  // first column past the run
+      const int twl = max(tw, min(tlast, (cend * BK) / kSub - 1));
       span = kWinEntries;
       // Ring of kDepth slots: sub-tile k lives in slot (k - tw) % kDepth.  While
       // sub-tile k is computed from registers, sub-tile k+1 is read from its
@@ -925,7 +954,7 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const Pre& s_pr
 #pragma unroll
       for (int t = 0; t < 4; ++t) o[4 * r + t] = s.acc[t][r];
 
-    const bool whole = (item_beg >= wbeg) && (item_end <= wend);
+    const bool whole = (real_beg >= wbeg) && (item_end <= wend);
     if (whole) {
       if (e == 0 && g < a.G) {
         const float f = bad ? NAN : a.v_scale / lsum;
@@ -933,11 +962,11 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const Pre& s_pr
         for (int i = 0; i < 16; ++i) o[i] *= f;
         store_bf16x16(a.out + (static_cast<int64_t>(b) * a.Hq + h * a.G + g) * kHeadDim + 16 * q, o);
       }
-    } else if (sc.of(item_end - 1) == sc.of(item_beg) + 1 &&
-               sc.of(item_beg) / kWavesPerWG == sc.of(item_end - 1) / kWavesPerWG) {
+    } else if (sc.of(item_end - 1) == sc.of(real_beg) + 1 &&
+               sc.of(real_beg) / kWavesPerWG == sc.of(item_end - 1) / kWavesPerWG) {
       // cut once, both pieces in this workgroup: hand off through LDS
-      const int cf = sc.of(item_beg), cl = cf + 1;
-      const int slot = (item_beg >= wbeg) ? 1 : 0;
+      const int cf = sc.of(real_beg), cl = cf + 1;
+      const int slot = (real_beg >= wbeg) ? 1 : 0;
       write_partial_lds(wg.part + (2 * (cid % kWavesPerWG) + slot) * kSlotFloats, o, s.m,
                         bad ? NAN : lsum, lane);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -953,8 +982,8 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const Pre& s_pr
                              wg.part + (2 * (cl % kWavesPerWG) + 0) * kSlotFloats});
       }
     } else {
-      const int cf = sc.of(item_beg), cl = sc.of(item_end - 1);
-      const int slot = (item_beg >= wbeg) ? 2 * cid + 1 : 2 * cid;
+      const int cf = sc.of(real_beg), cl = sc.of(item_end - 1);
+      const int slot = (real_beg >= wbeg) ? 2 * cid + 1 : 2 * cid;
       write_partial(a, slot, o, s.m, bad ? NAN : lsum, lane);
       wait_vm_stores();
       int old = 0;
@@ -985,7 +1014,7 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const Pre& s_pr
 // item line over the W waves, and the wave's share.
 template <int BK, bool WINDOWED, bool KP, bool ROPE, class Pre>
 __device__ __forceinline__ void run_shares(const AttnArgs& a, const Pre& pre, int B, int longest,
-                                           uint8_t* ring, const WgLocal wg) {
+                                           uint8_t* ring, const WgLocal wg, int64_t per_r) {
   const int tid = threadIdx.x;
   // rows with no work: +0 for inactive sequences, NaN for invalid positions
   for (int b = blockIdx.x; b < B; b += gridDim.x) {
@@ -1022,9 +1051,11 @@ __device__ __forceinline__ void run_shares(const AttnArgs& a, const Pre& pre, in
   if (whole_items) {
     const int64_t lo_w = first_item_start_at_or_after(pre, B, a.Hkv, cb);
     const int64_t hi_w = first_item_start_at_or_after(pre, B, a.Hkv, min(cb + per, total));
-    if (lo_w < hi_w) process_chunk<BK, WINDOWED, KP, ROPE>(a, pre, B, wid, sc, lo_w, hi_w, ring, wg);
+    if (lo_w < hi_w)
+      process_chunk<BK, WINDOWED, KP, ROPE>(a, pre, B, wid, sc, lo_w, hi_w, ring, wg, per_r);
   } else {
-    process_chunk<BK, WINDOWED, KP, ROPE>(a, pre, B, wid, sc, cb, min(cb + per, total), ring, wg);
+    process_chunk<BK, WINDOWED, KP, ROPE>(a, pre, B, wid, sc, cb, min(cb + per, total), ring, wg,
+                                          per_r);
   }
 }
 
@@ -1055,21 +1086,65 @@ __global__ void __launch_bounds__(kThreads, kWGPerCU * kWavesPerWG / 4) decode_a
       const int y = __shfl_up(x, off, kWave);
       if (lane >= off) x += y;
     }
-    int longest = n;
+    // each short item also counts its start cost (kItemCost)
+    int64_t per_r = 0;
+    int v = n, xv = x;
+    if constexpr (!WINDOWED) {
+      per_r = (static_cast<int64_t>(__builtin_amdgcn_readlane(x, kWave - 1)) * a.Hkv +
+               a.n_workers - 1) / a.n_workers;
+      if (__ballot(n > 0 && n < per_r) != 0) {  // some item is short: redo the prefix
+        v = (n > 0 && n < per_r) ? n + kItemCost : n;
+        xv = v;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+          const int y = __shfl_up(xv, off, kWave);
+          if (lane >= off) xv += y;
+        }
+      }
+    }
+    int longest = n;  // in real sub-tiles: decides whether items may be cut
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) longest = max(longest, __shfl_xor(longest, off));
-    const PreReg pre{x - n, __builtin_amdgcn_readlane(x, kWave - 1)};
-    run_shares<BK, WINDOWED, KP, ROPE>(a, pre, B, __builtin_amdgcn_readfirstlane(longest), ring, wg);
+    const PreReg pre{xv - v, __builtin_amdgcn_readlane(xv, kWave - 1)};
+    run_shares<BK, WINDOWED, KP, ROPE>(a, pre, B, __builtin_amdgcn_readfirstlane(longest), ring, wg,
+                                       per_r);
   } else {
     if (tid == 0) s_longest = 0;
     __syncthreads();
-    int longest = 0;
-    for (int b = tid; b < B; b += kThreads) {
-      int lo = 0;
-      bool inv;
-      const int n = seq_subtiles<BK, WINDOWED>(a, a.frame_pos[b], &lo, &inv);
-      s_pre[b] = n;
-      longest = max(longest, n);
+    int longest = 0;  // in real sub-tiles: decides whether items may be cut
+    int64_t per_r = 0;
+    if constexpr (WINDOWED) {
+      for (int b = tid; b < B; b += kThreads) {
+        int lo = 0;
+        bool inv;
+        const int n = seq_subtiles<BK, WINDOWED>(a, a.frame_pos[b], &lo, &inv);
+        s_pre[b] = n;
+        longest = max(longest, n);
+      }
+    } else {
+      constexpr int kPerThread = (kMaxBatch + kThreads - 1) / kThreads;
+      int nl[kPerThread];
+#pragma unroll
+      for (int k = 0; k < kPerThread; ++k) {
+        const int b = tid + k * kThreads;
+        nl[k] = 0;
+        if (b < B) {
+          int lo = 0;
+          bool inv;
+          nl[k] = seq_subtiles<BK, WINDOWED>(a, a.frame_pos[b], &lo, &inv);
+          s_pre[b] = nl[k];
+          longest = max(longest, nl[k]);
+        }
+      }
+      // each short item also counts its start cost (kItemCost): redo the prefix
+      __syncthreads();
+      block_exclusive_scan(s_pre, B);
+      per_r = (static_cast<int64_t>(s_pre[B]) * a.Hkv + a.n_workers - 1) / a.n_workers;
+#pragma unroll
+      for (int k = 0; k < kPerThread; ++k) {
+        const int b = tid + k * kThreads;
+        if (b < B) s_pre[b] = (nl[k] > 0 && nl[k] < per_r) ? nl[k] + kItemCost : nl[k];
+      }
     }
     // one LDS atomic per wave (64 lanes on one address would serialise)
 #pragma unroll
@@ -1078,7 +1153,7 @@ __global__ void __launch_bounds__(kThreads, kWGPerCU * kWavesPerWG / 4) decode_a
     __syncthreads();
     block_exclusive_scan(s_pre, B);
     run_shares<BK, WINDOWED, KP, ROPE>(a, PreLds{s_pre}, B,
-                                       __builtin_amdgcn_readfirstlane(s_longest), ring, wg);
+                                       __builtin_amdgcn_readfirstlane(s_longest), ring, wg, per_r);
   }
   wait_vmcnt<0>();  // no direct-to-LDS load outlives the wave
 }
