@@ -12,7 +12,10 @@ in GB/s; tokens/s is batch / step time.  The step is replayed as a HIP graph
 (inputs resident in HBM); a second, eager phase issues a step's full-layer
 launches back to back between two events on their stream to get the dominant
 kernel's average launch duration for the roofline (window layers likewise).  `cpu_baseline` times the CPU
-oracle on a bounded sample of the same workload.
+oracle on a bounded sample of the same workload.  `hbm_ceiling` is the best rate
+of the read probes of libpkv_probe on a 4 GiB buffer: one stream, and whole
+tiles of the kernel's tile size (block x head_dim bytes) in a scrambled order,
+over a few launch sizes with plain and non-temporal loads.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5]
     python bench.py --calibrate-copy      # plain device copy, for counter scaling
@@ -65,6 +68,44 @@ def calibrate_copy(steps):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"calibrate_copy_bytes": n, "launches": steps}), flush=True)
+
+
+def hbm_ceiling(dev, tile_bytes, reps=10, nbytes=1 << 32):
+    """Best read rates (GB/s) of the stream and tile probes, each launch timed
+    with events on torch's current stream, the one the probes launch on."""
+    import torch
+    from paged_fp8_kv_amd import probe as Q
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    buf.fill_(0x5A)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    best = {}
+    for kind in ("stream", "tiles"):
+        for nt in (0, 1):
+            for grid in (256, 512, 1024, 2048, 4096):
+                if kind == "stream":
+                    def run():
+                        return Q.pkv_probe_stream_read(buf, grid, nt, sink)
+                else:
+                    def run():
+                        return Q.pkv_probe_tile_read(buf, tile_bytes, grid, nt, sink)
+                for _ in range(2):
+                    n = run()
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record()
+                for _ in range(reps):
+                    run()
+                b.record()
+                torch.cuda.synchronize()
+                gbs = n * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+                if gbs > best.get(kind, (0.0,))[0]:
+                    best[kind] = (gbs, grid, nt)
+    del buf
+    torch.cuda.empty_cache()
+    return {"stream_read_GBps": round(best["stream"][0], 1),
+            "tile_read_GBps": round(best["tiles"][0], 1), "tile_bytes": tile_bytes,
+            "probe_bytes": nbytes,
+            "best_launch": {k: {"grid": v[1], "nontemporal": bool(v[2])} for k, v in best.items()}}
 
 
 def cpu_baseline(wl, bufs_dev, seconds):
@@ -135,6 +176,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the HBM read probes (stream and scrambled tiles)")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--tables", choices=["padded", "csr"], default="padded",
                     help="block tables as padded rows (default) or compressed page lists")
@@ -384,8 +427,14 @@ def main():
                      "kernel": f"decode_attn_kernel<{cfg.block}, false, {str(args.k_layout == 'packed').lower()}, {str(args.rope).lower()}> (full layers)",
                      "bytes_per_launch": full_bytes, "avg_launch_us": round(full_us, 2),
                      "swa_avg_launch_us": round(swa_us, 2) if swa_us else None},
+        "hbm_ceiling": None,
         "cpu_baseline": None,
     }
+    if not args.no_ceiling:
+        ceil = hbm_ceiling(dev, cfg.block * cfg.head_dim)
+        ceil["full_layer_frac_of_stream"] = round(achieved / ceil["stream_read_GBps"], 4)
+        ceil["full_layer_frac_of_tiles"] = round(achieved / ceil["tile_read_GBps"], 4)
+        result["hbm_ceiling"] = ceil
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, bufs, args.cpu_seconds)
     print(json.dumps(result), flush=True)

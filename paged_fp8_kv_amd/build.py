@@ -1,4 +1,5 @@
-"""Build libpkv.so (the C-ABI library with the gfx950 kernels) in place.
+"""Build libpkv.so (the C-ABI library with the gfx950 kernels) and
+libpkv_probe.so (the HBM read-bandwidth probes) in place.
 
     python -m paged_fp8_kv_amd.build [--verbose]
 
@@ -14,6 +15,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpkv.so")
 SOURCES = ["abi.cpp", "control.hip", "decode_attn.hip"]
+PROBE_LIB = os.path.join(HERE, "libpkv_probe.so")
+PROBE_SOURCES = ["hbm_probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -24,8 +27,13 @@ FLAGS = [
 
 
 def build(verbose: bool = False, extra=()) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, *extra, "-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
+    _build_one(PROBE_LIB, PROBE_SOURCES, verbose, ())
+    return _build_one(LIB, SOURCES, verbose, extra)
+
+
+def _build_one(lib, sources, verbose, extra) -> str:
+    tmp = lib + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *FLAGS, *extra, "-o", tmp] + [os.path.join(CSRC, s) for s in sources]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -37,8 +45,8 @@ def build(verbose: bool = False, extra=()) -> str:
         raise RuntimeError("hipcc failed:\n" + msg)
     if verbose and msg.strip():
         print(msg)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
