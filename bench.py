@@ -77,7 +77,7 @@ def hbm_ceiling(dev, tile_bytes, reps=10, nbytes=1 << 32):
     from paged_fp8_kv_amd import probe as Q
     buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     buf.fill_(0x5A)
-    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    sink = torch.zeros(4096, dtype=torch.int32, device=dev)
     best = {}
     for kind in ("stream", "tiles"):
         for nt in (0, 1):

@@ -13,8 +13,9 @@
  *
  * Conventions:
  *   - `src` and `sink` are DEVICE pointers owned by the caller; `src` is
- *     16-byte aligned; `sink` is one uint32 that the probe XORs with the XOR
- *     of every 32-bit word it read (clear it first to read that value back).
+ *     16-byte aligned; `sink` holds at least `grid` uint32 words: workgroup i
+ *     stores into sink[i] the XOR of every 32-bit word it read, so the XOR of
+ *     sink[0 .. grid) is the XOR of everything the launch read.
  *   - `stream` is a hipStream_t passed as void*; the launch is asynchronous.
  *   - Each call returns the number of bytes its launch reads (>= 0), or a
  *     negative status; on a negative status nothing was enqueued, except

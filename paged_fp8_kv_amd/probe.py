@@ -44,18 +44,18 @@ def _check(n, what):
     return n
 
 
-def _args(buf, sink):
+def _args(buf, sink, grid):
     if buf.device.type != "cuda" or sink.device.type != "cuda":
         raise ValueError("buffer and sink must be device tensors")
     if buf.dtype != torch.uint8 or not buf.is_contiguous():
         raise ValueError("buffer must be a contiguous uint8 tensor")
-    if sink.dtype != torch.int32 or sink.numel() < 1:
-        raise ValueError("sink must be an int32 tensor of at least one element")
+    if sink.dtype != torch.int32 or not sink.is_contiguous() or sink.numel() < grid:
+        raise ValueError("sink must be a contiguous int32 tensor of at least `grid` elements")
     return buf.data_ptr(), buf.numel(), sink.data_ptr(), torch.cuda.current_stream().cuda_stream
 
 
 def pkv_probe_stream_read(buf, grid, nontemporal, sink):
-    p, n, s, st = _args(buf, sink)
+    p, n, s, st = _args(buf, sink, grid)
     return _check(lib().pkv_probe_stream_read(p, n, grid, int(bool(nontemporal)), s, st),
                   "pkv_probe_stream_read")
 
@@ -65,6 +65,6 @@ def pkv_probe_tile_read_bytes(nbytes, tile_bytes, grid):
 
 
 def pkv_probe_tile_read(buf, tile_bytes, grid, nontemporal, sink):
-    p, n, s, st = _args(buf, sink)
+    p, n, s, st = _args(buf, sink, grid)
     return _check(lib().pkv_probe_tile_read(p, n, tile_bytes, grid, int(bool(nontemporal)), s, st),
                   "pkv_probe_tile_read")
