@@ -12,7 +12,7 @@ in GB/s; tokens/s is batch / step time.  The step is replayed as a HIP graph
 (inputs resident in HBM); a second, eager phase issues a step's full-layer
 launches back to back between two events on their stream to get the dominant
 kernel's average launch duration for the roofline (window layers likewise).  `cpu_baseline` times the CPU
-oracle on a bounded sample of the same workload.  `hbm_ceiling` is the best rate
+oracle on a bounded sample of the same workload (before the GPU timing).  `hbm_ceiling` is the best rate
 of the read probes of libpkv_probe on a 4 GiB buffer: one stream, and whole
 tiles of the kernel's tile size (block x head_dim bytes) in a scrambled order,
 over a few launch sizes with plain and non-temporal loads.
@@ -299,6 +299,14 @@ def main():
         for i in range(cfg.layers):
             layer(i)
 
+    # The CPU baseline runs before any GPU timing: besides being cheap to place
+    # here, its seconds of host work let the device settle after whatever ran
+    # before this process (another process freeing ~100 GB of device memory
+    # was measured to slow this step by ~4% for about 20 s).
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, bufs, args.cpu_seconds)
+
     # eager warm-up; after the first step the cache holds this step's tokens,
     # so every later step recomputes identical outputs
     for _ in range(max(args.warmup, 1)):
@@ -435,8 +443,7 @@ def main():
         ceil["full_layer_frac_of_stream"] = round(achieved / ceil["stream_read_GBps"], 4)
         ceil["full_layer_frac_of_tiles"] = round(achieved / ceil["tile_read_GBps"], 4)
         result["hbm_ceiling"] = ceil
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, bufs, args.cpu_seconds)
+    result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
 
 

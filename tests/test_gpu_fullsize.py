@@ -39,6 +39,11 @@ def _run(name, rows_fn, layers, gpu):
         assert np.array_equal(after[j], before[j]), \
             f"{name} buffer {j}: {int((after[j] != before[j]).sum())} bytes differ"
     print(f"[fullsize] {name}: max abs err {worst:.2e}", flush=True)
+    # hand the pool back now: the driver's clean-up of tens of GB of freed
+    # device memory slows later bandwidth-bound work for some seconds, so let
+    # it overlap the rest of the session rather than what runs after it
+    del bufs, outs
+    torch.cuda.empty_cache()
 
 
 def test_fullsize_36_layer_batch64(gpu):
