@@ -190,7 +190,9 @@ int64_t pkv_decode_workspace_bytes(int32_t batch, int32_t q_heads, int32_t kv_he
  * max(0, frame_pos-window+1); key t lives in block block_table[b, t/block] at
  * slot t%block.  out bf16 [batch, q_heads, head_dim] =
  * softmax(sm_scale * q.K^) V^ with K^ = decode(K)*k_scale, V^ = decode(V)*v_scale,
- * accumulated in fp32 and rounded to bf16.
+ * accumulated in fp32 and rounded to bf16.  k_scale, v_scale and sm_scale are
+ * finite and > 0, and so is the fp32 product sm_scale * k_scale * log2(e)
+ * (else PKV_ERR_ARG).
  * k_packed: 1 = the K half in the packed view [nb, Hkv, block/2, head_dim, 2]
  * (two tokens interleaved per dimension), 0 = token-major rows
  * [nb, Hkv, block, head_dim] like V ("KV-cache layout"); same bytes, same speed.

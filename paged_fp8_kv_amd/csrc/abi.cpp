@@ -301,6 +301,13 @@ static int attn_impl(int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t h
   if (!(k_scale > 0.f) || !(v_scale > 0.f) || !(sm_scale > 0.f) || k_scale == INFINITY ||
       v_scale == INFINITY || sm_scale == INFINITY)
     return fail(PKV_ERR_ARG, "scales must be finite and > 0");
+  {
+    // the kernel scales scores by this product (log2 domain): it must be a
+    // finite positive float for the softmax to be defined
+    const float ss = sm_scale * k_scale * 1.4426950408889634f;
+    if (!(ss > 0.f) || ss == INFINITY)
+      return fail(PKV_ERR_ARG, "sm_scale * k_scale must be a finite positive float");
+  }
   const int ms = pkv::attn_max_subtiles(block, table_width, window);
   const int w = pkv::attn_workers(batch, kv_heads, ms);
   const int64_t need = pkv::attn_workspace_bytes(batch, kv_heads, w);

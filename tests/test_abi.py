@@ -63,6 +63,10 @@ def test_attention_argument_errors():
     assert _attn(width=5) == P.PKV_ERR_ARG                 # stride < width
     assert _attn() == P.PKV_ERR_ARG                        # null pointers
     assert _attn(batch=0) == P.PKV_OK                      # empty batch is a no-op
+    fake = dict(q=0x1000, k=0x1000, v=0x1000, table=0x1000, pos=0x1000, out=0x1000)
+    assert _attn(ks=1e30, sm=1e30, **fake) == P.PKV_ERR_ARG   # product overflows fp32
+    assert _attn(ks=1e-30, sm=1e-30, **fake) == P.PKV_ERR_ARG  # product underflows to 0
+    assert b"sm_scale * k_scale" in P.lib().pkv_last_error()
 
 
 def test_rope_argument_errors():
