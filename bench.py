@@ -33,7 +33,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCES = ["paged_fp8_kv_amd/csrc/decode_attn.hip", "paged_fp8_kv_amd/csrc/pkv_device.hpp"]
+# what decides the dominant kernel's code: its sources and the build flags
+KERNEL_SOURCES = ["paged_fp8_kv_amd/csrc/decode_attn.hip", "paged_fp8_kv_amd/csrc/pkv_device.hpp",
+                  "paged_fp8_kv_amd/build.py"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_attn_full_cfg3_traffic.json")
 
 
