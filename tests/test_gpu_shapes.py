@@ -1,0 +1,63 @@
+"""Parity against the oracle across the supported shapes that the benchmark
+configurations leave out: query/KV group sizes 1, 2, 4 and 8, blocks of 16,
+64 and 128 tokens, batches on both sides of the 64-sequence register prefix
+up to the largest supported batch, contexts of one token, contexts that end
+mid-block or just past the window, inactive rows and an all-inactive batch.
+Each case runs the alternating window/full layer pair through the layer entry
+point; the written cache is compared byte for byte, the outputs within the
+attention tolerance."""
+import numpy as np
+import pytest
+
+import workloads as W
+from gpu_harness import assert_close, gpu_step, oracle_step, poison_stale
+from workloads import Config
+
+pytestmark = pytest.mark.gpu
+
+PAIR = ("swa", "full")
+CASES = [
+    # name,                  hq, hkv, block, batch, contexts,      inactive, seed
+    ("g1_bk16_b3_L1-300", 4, 4, 16, 3, ("uniform", 1, 300), 0, 11),
+    ("g2_bk64_b70_L1-700", 8, 4, 64, 70, ("uniform", 1, 700), 5, 12),
+    ("g4_bk128_b5_L100-1500", 8, 2, 128, 5, ("uniform", 100, 1500), 0, 13),
+    ("g8_bk64_b2_L129", 16, 2, 64, 2, ("fixed", 129), 0, 14),
+    ("g8_bk16_b8192_L1-40", 8, 1, 16, 8192, ("uniform", 1, 40), 100, 15),
+]
+
+
+def _run(cfg, gpu):
+    wl = W.make_workload(cfg)
+    host = W.make_buffers(wl, "cpu")
+    poison_stale(host, wl)
+    snaps = [h.numpy().copy() for h in host]
+    bufs = [h.to(gpu) for h in host]
+    print(f"[shapes] {cfg.name}: nb={wl.nb}", flush=True)
+    outs, _ = gpu_step(wl, bufs, gpu)
+    ref, _ = oracle_step(wl, snaps)  # brings `snaps` to the post-step cache
+    for j, b in enumerate(bufs):
+        got = b.cpu().numpy()
+        assert np.array_equal(got, snaps[j]), \
+            f"{cfg.name} buffer {j}: {int((got != snaps[j]).sum())} bytes differ"
+    return wl, outs, ref
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_shapes_match_oracle(case, gpu):
+    name, hq, hkv, block, batch, ctx, inactive, seed = case
+    cfg = Config(name, PAIR, batch, hq, hkv, 64, block, ctx, seed=seed, n_inactive=inactive,
+                 max_ctx=ctx[-1])
+    wl, outs, ref = _run(cfg, gpu)
+    for i in range(cfg.layers):
+        assert_close(outs[i], ref[i], f"{name} layer {i}")
+
+
+def test_all_inactive_batch(gpu):
+    """No sequence has work: every output row is +0 and the cache is untouched."""
+    cfg = Config("inactive_b4", PAIR, 4, 8, 1, 64, 32, ("uniform", 1, 100), seed=7,
+                 n_inactive=4, max_ctx=100)
+    wl, outs, ref = _run(cfg, gpu)
+    for i in range(cfg.layers):
+        o = outs[i].float().cpu().numpy()
+        assert np.array_equal(o, np.zeros_like(o)) and not np.signbit(o).any(), f"layer {i}"
+        assert np.array_equal(ref[i], np.zeros_like(ref[i]))
