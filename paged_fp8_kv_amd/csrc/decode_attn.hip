@@ -775,7 +775,8 @@ struct WgLocal {
 template <int BK, bool WINDOWED, bool KP, bool ROPE, class Pre>
 __device__ __forceinline__ void process_chunk(const AttnArgs& a, const Pre& s_pre, int B, int cid,
                                               const Sched sc, int64_t cur, int64_t wend,
-                                              uint8_t* ring, const WgLocal wg, int64_t per_r) {
+                                              uint8_t* ring, const WgLocal wg, int64_t per_r,
+                                              int half) {
   const int lane = lane_id();
   const int m = lane & 15, q = lane >> 4, e = m >> 3, g = m & 7;
   const int64_t wbeg = cur;
@@ -791,7 +792,6 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const Pre& s_pr
     const int pre_b = __builtin_amdgcn_readfirstlane(s_pre(b));
     const int seg = static_cast<int>(min(static_cast<int64_t>(n - j), wend - cur));
     const int64_t item_beg = static_cast<int64_t>(pre_b) * a.Hkv + static_cast<int64_t>(h) * n;
-    const int64_t item_end = item_beg + n;
     // The item's frame position, its first table window and its queries are
     // loaded together.  Without a window the keys start at 0, so the first
     // sub-tile (j) and its table window do not depend on the position.
@@ -799,7 +799,10 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const Pre& s_pr
     Item<BK, WINDOWED, KP> it(a, b, h);
     // without a window: the window must hold column jr*kSub/BK; only an item
     // shorter than a share can carry a start cost (jr = j - kItemCost)
-    if (!WINDOWED) it.load_window(((n < per_r + kItemCost ? max(j - kItemCost, 0) : j) * kSub) / BK);
+    // (in halves mode the whole item, at most kTinyItem sub-tiles, is inside a
+    // window from column 0)
+    if (!WINDOWED)
+      it.load_window(half > 0 ? 0 : ((n < per_r + kItemCost ? max(j - kItemCost, 0) : j) * kSub) / BK);
     u32x4_t q0 = {0u, 0u, 0u, 0u}, q1 = {0u, 0u, 0u, 0u};
     if (g < a.G) {
       const uint16_t* qp = a.q + (static_cast<int64_t>(b) * a.Hq + h * a.G + g) * kHeadDim + 16 * q;
@@ -834,14 +837,18 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const Pre& s_pr
     const int hi = __builtin_amdgcn_readfirstlane(fp_raw);
     const int lo = WINDOWED ? max(0, hi - a.window + 1) : 0;
     it.set_range(lo, hi);
-    // On the line the item holds its start cost c0 (0 or kItemCost) first,
-    // then its sub-tiles: this piece's sub-tiles are [jr, jr + segr).
-    const int c0 = n - (hi / kSub - lo / kSub + 1);
+    // On the line the item holds c0 virtual sub-tiles (a start cost of 0 or
+    // kItemCost, or in halves mode the padding that centres its sub-tiles on
+    // the boundary of its two shares), then its nr sub-tiles, then (halves
+    // mode only) trailing padding: this piece's sub-tiles are [jr, jr + segr).
+    const int nr = hi / kSub - lo / kSub + 1;
+    const int c0 = half > 0 ? half - (nr + 1) / 2 : n - nr;
     const int jr = max(j - c0, 0);
-    const int segr = max(0, j + seg - c0 - jr);
+    const int segr = min(max(0, j + seg - c0 - jr), nr - jr);
     const int64_t real_beg = item_beg + c0;  // where the item's sub-tiles start on the line
-    if (segr == 0) {
-      // the piece covers only the start cost: no keys, no partial
+    const int64_t real_end = real_beg + nr;  // ... and end
+    if (segr <= 0) {
+      // the piece covers only virtual sub-tiles: no keys, no partial
       cur += seg;
       j = 0;
       if (++h == a.Hkv) {
@@ -954,7 +961,7 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const Pre& s_pr
 #pragma unroll
       for (int t = 0; t < 4; ++t) o[4 * r + t] = s.acc[t][r];
 
-    const bool whole = (real_beg >= wbeg) && (item_end <= wend);
+    const bool whole = (real_beg >= wbeg) && (real_end <= wend);
     if (whole) {
       if (e == 0 && g < a.G) {
         const float f = bad ? NAN : a.v_scale / lsum;
@@ -962,8 +969,8 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const Pre& s_pr
         for (int i = 0; i < 16; ++i) o[i] *= f;
         store_bf16x16(a.out + (static_cast<int64_t>(b) * a.Hq + h * a.G + g) * kHeadDim + 16 * q, o);
       }
-    } else if (sc.of(item_end - 1) == sc.of(real_beg) + 1 &&
-               sc.of(real_beg) / kWavesPerWG == sc.of(item_end - 1) / kWavesPerWG) {
+    } else if (sc.of(real_end - 1) == sc.of(real_beg) + 1 &&
+               sc.of(real_beg) / kWavesPerWG == sc.of(real_end - 1) / kWavesPerWG) {
       // cut once, both pieces in this workgroup: hand off through LDS
       const int cf = sc.of(real_beg), cl = cf + 1;
       const int slot = (real_beg >= wbeg) ? 1 : 0;
@@ -982,7 +989,7 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const Pre& s_pr
                              wg.part + (2 * (cl % kWavesPerWG) + 0) * kSlotFloats});
       }
     } else {
-      const int cf = sc.of(real_beg), cl = sc.of(item_end - 1);
+      const int cf = sc.of(real_beg), cl = sc.of(real_end - 1);
       const int slot = (real_beg >= wbeg) ? 2 * cid + 1 : 2 * cid;
       write_partial(a, slot, o, s.m, bad ? NAN : lsum, lane);
       wait_vm_stores();
@@ -1010,11 +1017,23 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const Pre& s_pr
   }
 }
 
+// Items of at most kTinyItem sub-tiles are split between two waves of one
+// workgroup (two shares of `half` sub-tiles each, the item's sub-tiles centred
+// on their boundary, the two pieces merged through LDS) when the launch has
+// two waves per item: each wave's dependent chain of set-up loads, K/V loads
+// and sub-tiles is then about half as long.  Full and window launches decide
+// alike, so a window launch over contexts that fit the window reproduces the
+// full launch bit for bit.
+__device__ __forceinline__ bool halves_fit(int longest, int64_t items, int workers) {
+  return longest >= 2 && longest <= kTinyItem && 2 * items <= workers;
+}
+
 // Everything after the prefix: rows without work, the static split of the
 // item line over the W waves, and the wave's share.
 template <int BK, bool WINDOWED, bool KP, bool ROPE, class Pre>
 __device__ __forceinline__ void run_shares(const AttnArgs& a, const Pre& pre, int B, int longest,
-                                           uint8_t* ring, const WgLocal wg, int64_t per_r) {
+                                           uint8_t* ring, const WgLocal wg, int64_t per_r,
+                                           int half) {
   const int tid = threadIdx.x;
   // rows with no work: +0 for inactive sequences, NaN for invalid positions
   for (int b = blockIdx.x; b < B; b += gridDim.x) {
@@ -1037,9 +1056,11 @@ __device__ __forceinline__ void run_shares(const AttnArgs& a, const Pre& pre, in
   if (total == 0) return;
   const int W = a.n_workers;
   const int wid = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerWG + (tid >> 6));
-  const int64_t per = (total + W - 1) / W;
+  // halves mode: every item is exactly two shares of `half` sub-tiles
+  const int64_t per = half > 0 ? half : (total + W - 1) / W;
   const int64_t cb = static_cast<int64_t>(wid) * per;
-  const bool whole_items = longest <= kTinyItem || 2 * static_cast<int64_t>(longest) <= per;
+  const bool whole_items =
+      half == 0 && (longest <= kTinyItem || 2 * static_cast<int64_t>(longest) <= per);
   if (!whole_items) {
     // items may be cut: clear the workgroup's LDS arrival counters (every
     // wave of the workgroup gets here; the decision is the same for all)
@@ -1052,10 +1073,10 @@ __device__ __forceinline__ void run_shares(const AttnArgs& a, const Pre& pre, in
     const int64_t lo_w = first_item_start_at_or_after(pre, B, a.Hkv, cb);
     const int64_t hi_w = first_item_start_at_or_after(pre, B, a.Hkv, min(cb + per, total));
     if (lo_w < hi_w)
-      process_chunk<BK, WINDOWED, KP, ROPE>(a, pre, B, wid, sc, lo_w, hi_w, ring, wg, per_r);
+      process_chunk<BK, WINDOWED, KP, ROPE>(a, pre, B, wid, sc, lo_w, hi_w, ring, wg, per_r, 0);
   } else {
     process_chunk<BK, WINDOWED, KP, ROPE>(a, pre, B, wid, sc, cb, min(cb + per, total), ring, wg,
-                                          per_r);
+                                          per_r, half);
   }
 }
 
@@ -1063,6 +1084,7 @@ template <int BK, bool WINDOWED, bool KP, bool ROPE>
 __global__ void __launch_bounds__(kThreads, kWGPerCU * kWavesPerWG / 4) decode_attn_kernel(AttnArgs a) {
   extern __shared__ int s_pre[];  // [B + 1] prefix of per-sequence sub-tile counts
   __shared__ int s_longest;       // longest item, in sub-tiles
+  __shared__ int s_active;        // sequences with work (window launches)
   __shared__ __attribute__((aligned(16))) uint8_t s_ring[kWavesPerWG * kDepth * kSlotBytes];
   __shared__ __attribute__((aligned(16))) float s_part[kWavesPerWG * 2 * kSlotFloats];
   __shared__ int s_cnt[kWavesPerWG];
@@ -1086,33 +1108,53 @@ __global__ void __launch_bounds__(kThreads, kWGPerCU * kWavesPerWG / 4) decode_a
       const int y = __shfl_up(x, off, kWave);
       if (lane >= off) x += y;
     }
-    // each short item also counts its start cost (kItemCost)
+    int longest = n;  // in real sub-tiles: decides whether items may be cut
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) longest = max(longest, __shfl_xor(longest, off));
+    longest = __builtin_amdgcn_readfirstlane(longest);
+    const uint64_t am = __ballot(n > 0);  // sequences with work
+    const int64_t items = static_cast<int64_t>(__popcll(am)) * a.Hkv;
     int64_t per_r = 0;
+    int half = 0;
     int v = n, xv = x;
-    if constexpr (!WINDOWED) {
+    bool rescan = false;
+    if (halves_fit(longest, items, a.n_workers)) {
+      // every item with work is 2*half long on the line: the prefix is that
+      // times the number of such sequences before this lane
+      half = (longest + 1) / 2;
+      const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(am >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(am), 0));
+      v = n > 0 ? 2 * half : 0;
+      xv = 2 * half * below + v;
+    } else if constexpr (!WINDOWED) {
+      // each short item also counts its start cost (kItemCost)
       per_r = (static_cast<int64_t>(__builtin_amdgcn_readlane(x, kWave - 1)) * a.Hkv +
                a.n_workers - 1) / a.n_workers;
       if (__ballot(n > 0 && n < per_r) != 0) {  // some item is short: redo the prefix
         v = (n > 0 && n < per_r) ? n + kItemCost : n;
-        xv = v;
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-          const int y = __shfl_up(xv, off, kWave);
-          if (lane >= off) xv += y;
-        }
+        rescan = true;
       }
     }
-    int longest = n;  // in real sub-tiles: decides whether items may be cut
+    if (rescan) {
+      xv = v;
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) longest = max(longest, __shfl_xor(longest, off));
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int y = __shfl_up(xv, off, kWave);
+        if (lane >= off) xv += y;
+      }
+    }
     const PreReg pre{xv - v, __builtin_amdgcn_readlane(xv, kWave - 1)};
-    run_shares<BK, WINDOWED, KP, ROPE>(a, pre, B, __builtin_amdgcn_readfirstlane(longest), ring, wg,
-                                       per_r);
+    run_shares<BK, WINDOWED, KP, ROPE>(a, pre, B, longest, ring, wg, per_r, half);
   } else {
-    if (tid == 0) s_longest = 0;
+    if (tid == 0) {
+      s_longest = 0;
+      s_active = 0;
+    }
     __syncthreads();
     int longest = 0;  // in real sub-tiles: decides whether items may be cut
-    int64_t per_r = 0;
+    int active = 0;   // sequences with work
+    constexpr int kPerThread = WINDOWED ? 1 : (kMaxBatch + kThreads - 1) / kThreads;
+    int nl[kPerThread];  // full launches keep their counts for the rewrites below
     if constexpr (WINDOWED) {
       for (int b = tid; b < B; b += kThreads) {
         int lo = 0;
@@ -1120,10 +1162,9 @@ __global__ void __launch_bounds__(kThreads, kWGPerCU * kWavesPerWG / 4) decode_a
         const int n = seq_subtiles<BK, WINDOWED>(a, a.frame_pos[b], &lo, &inv);
         s_pre[b] = n;
         longest = max(longest, n);
+        active += n > 0;
       }
     } else {
-      constexpr int kPerThread = (kMaxBatch + kThreads - 1) / kThreads;
-      int nl[kPerThread];
 #pragma unroll
       for (int k = 0; k < kPerThread; ++k) {
         const int b = tid + k * kThreads;
@@ -1134,10 +1175,32 @@ __global__ void __launch_bounds__(kThreads, kWGPerCU * kWavesPerWG / 4) decode_a
           nl[k] = seq_subtiles<BK, WINDOWED>(a, a.frame_pos[b], &lo, &inv);
           s_pre[b] = nl[k];
           longest = max(longest, nl[k]);
+          active += nl[k] > 0;
         }
       }
-      // each short item also counts its start cost (kItemCost): redo the prefix
+    }
+    // one LDS atomic per wave and quantity (64 lanes on one address would
+    // serialise)
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      longest = max(longest, __shfl_xor(longest, off));
+      active += __shfl_xor(active, off);
+    }
+    if ((tid & 63) == 0) {
+      atomicMax(&s_longest, longest);
+      atomicAdd(&s_active, active);
+    }
+    __syncthreads();
+    const int lg = __builtin_amdgcn_readfirstlane(s_longest);
+    const int64_t items = static_cast<int64_t>(s_active) * a.Hkv;
+    int64_t per_r = 0;
+    int half = 0;
+    if (halves_fit(lg, items, a.n_workers)) {
+      half = (lg + 1) / 2;
+      for (int b = tid; b < B; b += kThreads) s_pre[b] = s_pre[b] > 0 ? 2 * half : 0;
       __syncthreads();
+    } else if constexpr (!WINDOWED) {
+      // each short item also counts its start cost (kItemCost): redo the prefix
       block_exclusive_scan(s_pre, B);
       per_r = (static_cast<int64_t>(s_pre[B]) * a.Hkv + a.n_workers - 1) / a.n_workers;
 #pragma unroll
@@ -1145,15 +1208,10 @@ __global__ void __launch_bounds__(kThreads, kWGPerCU * kWavesPerWG / 4) decode_a
         const int b = tid + k * kThreads;
         if (b < B) s_pre[b] = (nl[k] > 0 && nl[k] < per_r) ? nl[k] + kItemCost : nl[k];
       }
+      __syncthreads();
     }
-    // one LDS atomic per wave (64 lanes on one address would serialise)
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) longest = max(longest, __shfl_xor(longest, off));
-    if ((tid & 63) == 0) atomicMax(&s_longest, longest);
-    __syncthreads();
     block_exclusive_scan(s_pre, B);
-    run_shares<BK, WINDOWED, KP, ROPE>(a, PreLds{s_pre}, B,
-                                       __builtin_amdgcn_readfirstlane(s_longest), ring, wg, per_r);
+    run_shares<BK, WINDOWED, KP, ROPE>(a, PreLds{s_pre}, B, lg, ring, wg, per_r, half);
   }
   wait_vmcnt<0>();  // no direct-to-LDS load outlives the wave
 }
@@ -1187,7 +1245,9 @@ hipError_t launch_bk(const AttnArgs& a, bool win, bool kp, int n_wg, size_t lds,
 int attn_workers(int64_t batch, int kv_heads, int max_subtiles) {
   const int64_t total = batch * kv_heads * static_cast<int64_t>(max_subtiles);
   int64_t w = (total + kMinSubtilesPerWorker - 1) / kMinSubtilesPerWorker;
-  if (w < batch * kv_heads) w = batch * kv_heads;  // short items: one wave each
+  // short items: up to two waves each (window launches split each item
+  // between two waves of one workgroup when the launch has them)
+  if (w < 2 * batch * kv_heads) w = 2 * batch * kv_heads;
   w = (w + kWavesPerWG - 1) / kWavesPerWG * kWavesPerWG;
   if (w < kWavesPerWG) w = kWavesPerWG;
   if (w > kMaxWorkers) w = kMaxWorkers / kWavesPerWG * kWavesPerWG;
