@@ -47,9 +47,13 @@ constexpr int kWavesPerWG = PKV_WAVES_PER_WG;
 constexpr int kThreads = 64 * kWavesPerWG;
 constexpr float kRescaleSlack = 8.0f; // log2 units
 #ifndef PKV_DEPTH
-#define PKV_DEPTH 6
+#define PKV_DEPTH 4
 #endif
-constexpr int kDepth = PKV_DEPTH;     // sub-tiles in flight per wave
+// Sub-tiles in flight per wave.  Measured with the accumulators in VGPRs:
+// 4 beats 6 by 1-1.5 us per full layer of the batch-64 x 8192 step (less
+// queueing in the memory system for the same rate), 8 is 1 us slower, 2
+// starves the stream (134 us).
+constexpr int kDepth = PKV_DEPTH;
 constexpr int kTinyItem = 8;          // items this short (sub-tiles) are never split
 // Fixed cost of starting a short item (shorter than a share), in sub-tiles:
 // the wait for its set-up loads and first K/V loads plus the fill and drain
