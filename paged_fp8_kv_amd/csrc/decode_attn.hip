@@ -142,16 +142,11 @@ __device__ __forceinline__ void block_exclusive_scan(int* s, int n) {
 }
 
 // Cross-workgroup hand-off of split-KV partials.  Partials are written and
-// read with agent-scope relaxed atomics (write-through / coherent accesses),
-// and the writer waits for its stores to complete before it bumps the arrival
-// counter.  This avoids agent-scope release/acquire fences, which on this
-// target write back and invalidate the whole L2 of the issuing XCD.
-__device__ __forceinline__ void st_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_coherent(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+// read with device-coherent buffer accesses (write-through stores, loads that
+// miss a stale L2 line; see write_partial and SlotPieces), and the writer
+// waits for its stores to complete before it bumps the arrival counter.  This
+// avoids agent-scope release/acquire fences, which on this target write back
+// and invalidate the whole L2 of the issuing XCD.
 __device__ __forceinline__ void wait_vm_stores() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): every issued store has completed
@@ -179,13 +174,8 @@ struct State {
   bool bad;        // a table entry outside [0, nb) was met
 };
 
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
 // dword 3 of a raw (untyped, unswizzled) buffer resource on this target
 constexpr int kRsrcWord3 = 0x00020000;
-__device__ __forceinline__ rsrc_t tile_rsrc(const uint8_t* p, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p), static_cast<short>(0), bytes,
-                                           kRsrcWord3);
-}
 
 struct Stage {
   u32x4_t k0, k1;   // 32 bytes of packed K row (pair m), bytes [32q, 32q+32)
