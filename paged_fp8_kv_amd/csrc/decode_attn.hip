@@ -631,10 +631,11 @@ struct LdsPieces {
 };
 
 // Combine the P pieces of item (b, h), in piece order, and write the output
-// row.  Eight pieces are fetched per round; lane (g = lane & 7, part =
-// lane >> 3) owns dims 8*part .. 8*part+7 of head g.  Rounds combine with a
-// running maximum.
-template <class Src>
+// row.  ROUND pieces are fetched per round (8 from the workspace; the two LDS
+// pieces of an item cut inside one workgroup in a single round of 2); lane
+// (g = lane & 7, part = lane >> 3) owns dims 8*part .. 8*part+7 of head g.
+// Rounds combine with a running maximum.
+template <int ROUND, class Src>
 __device__ __forceinline__ void merge_item(const AttnArgs& a, int b, int h, int P, int lane,
                                            const Src& src) {
   const int g = lane & 7, part = lane >> 3;
@@ -642,21 +643,21 @@ __device__ __forceinline__ void merge_item(const AttnArgs& a, int b, int h, int 
   float acc[8];
 #pragma unroll
   for (int d = 0; d < 8; ++d) acc[d] = 0.f;
-  for (int k0 = 0; k0 < P; k0 += 8) {
-    float mk[8], lk[8];
-    u32x4_t o0[8], o1[8];
+  for (int k0 = 0; k0 < P; k0 += ROUND) {
+    float mk[ROUND], lk[ROUND];
+    u32x4_t o0[ROUND], o1[ROUND];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) src.load(min(k0 + i, P - 1), g, part, mk[i], lk[i], o0[i], o1[i]);
+    for (int i = 0; i < ROUND; ++i) src.load(min(k0 + i, P - 1), g, part, mk[i], lk[i], o0[i], o1[i]);
     float mx = mrun;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < ROUND; ++i)
       if (k0 + i < P) mx = fmaxf(mx, mk[i]);
     const float sc = __builtin_amdgcn_exp2f(mrun - mx);
     lrun *= sc;
 #pragma unroll
     for (int d = 0; d < 8; ++d) acc[d] *= sc;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < ROUND; ++i) {
       if (k0 + i < P) {
         const float w = __builtin_amdgcn_exp2f(mk[i] - mx);
         lrun += w * lk[i];
@@ -978,9 +979,9 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const Pre& s_pr
       old = __builtin_amdgcn_readfirstlane(__shfl(old, 0, 64));
       if (old == 1) {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-        merge_item(a, b, h, 2, lane,
-                   LdsPieces{wg.part + (2 * (cf % kWavesPerWG) + 1) * kSlotFloats,
-                             wg.part + (2 * (cl % kWavesPerWG) + 0) * kSlotFloats});
+        merge_item<2>(a, b, h, 2, lane,
+                      LdsPieces{wg.part + (2 * (cf % kWavesPerWG) + 1) * kSlotFloats,
+                                wg.part + (2 * (cl % kWavesPerWG) + 0) * kSlotFloats});
       }
     } else {
       const int cf = sc.of(real_beg), cl = sc.of(real_end - 1);
@@ -994,7 +995,7 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const Pre& s_pr
       const int ncontrib = cl - cf + 1;
       if (old == ncontrib - 1) {
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        merge_item(a, b, h, ncontrib, lane, SlotPieces{partial_rsrc(a), cf});
+        merge_item<8>(a, b, h, ncontrib, lane, SlotPieces{partial_rsrc(a), cf});
         if (lane == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
