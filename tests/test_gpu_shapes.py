@@ -2,7 +2,8 @@
 configurations leave out: query/KV group sizes 1, 2, 4 and 8, blocks of 16,
 64 and 128 tokens, batches on both sides of the 64-sequence register prefix
 up to the largest supported batch, contexts of one token, contexts that end
-mid-block or just past the window, inactive rows and an all-inactive batch.
+mid-block or just past the window, tiny items split between two waves,
+inactive rows and an all-inactive batch.
 Each case runs the alternating window/full layer pair through the layer entry
 point; the written cache is compared byte for byte, the outputs within the
 attention tolerance."""
@@ -23,6 +24,11 @@ CASES = [
     ("g4_bk128_b5_L100-1500", 8, 2, 128, 5, ("uniform", 100, 1500), 0, 13),
     ("g8_bk64_b2_L129", 16, 2, 64, 2, ("fixed", 129), 0, 14),
     ("g8_bk16_b8192_L1-40", 8, 1, 16, 8192, ("uniform", 1, 40), 100, 15),
+    # items of 1-3 sub-tiles split between two waves: a 1-sub-tile item's second
+    # share holds only padding, a 2-sub-tile item has padding on both sides,
+    # a 3-sub-tile item splits 2 + 1 (register prefix, then LDS prefix)
+    ("g8_bk16_b40_L1-70_halves", 16, 2, 16, 40, ("uniform", 1, 70), 3, 16),
+    ("g4_bk16_b100_L1-70_halves", 16, 4, 16, 100, ("uniform", 1, 70), 7, 17),
 ]
 
 
