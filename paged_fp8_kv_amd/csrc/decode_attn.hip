@@ -32,6 +32,8 @@
 //    beats it by more than 2^8, so rescaling is rare and the PV weights stay
 //    below 256 (exact bookkeeping: numerator and denominator share the
 //    reference maximum).
+#include <atomic>
+
 #include "pkv_device.hpp"
 #include "pkv_internal.hpp"
 
@@ -1300,13 +1302,15 @@ hipError_t launch_decode_attn(const AttnLaunch& L, hipStream_t stream) {
   // the workspace holds partial slots for at most this many workers
   if (a.n_workers < kWavesPerWG || a.n_workers > kMaxWorkers || a.n_workers % kWavesPerWG)
     return hipErrorInvalidValue;
-  // never launch more workers than can be resident together
-  static int cu_count[64];
+  // never launch more workers than can be resident together (the CU count
+  // of each device is cached; concurrent callers may both query it)
+  static std::atomic<int> cu_count[64];
   int dev = 0;
   if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
-    if (!cu_count[dev])
-      (void)hipDeviceGetAttribute(&cu_count[dev], hipDeviceAttributeMultiprocessorCount, dev);
-    const int resident = cu_count[dev] * kWGPerCU * kWavesPerWG;
+    int cus = cu_count[dev].load(std::memory_order_relaxed);
+    if (!cus && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+      cu_count[dev].store(cus, std::memory_order_relaxed);
+    const int resident = cus * kWGPerCU * kWavesPerWG;
     if (resident >= kWavesPerWG && a.n_workers > resident) a.n_workers = resident;
   }
   const int n_wg = a.n_workers / kWavesPerWG;
