@@ -689,6 +689,8 @@ __device__ __forceinline__ void merge_item(const AttnArgs& a, int b, int h, int 
 struct PreLds {
   const int* s;
   __device__ __forceinline__ int operator()(int i) const { return s[i]; }
+  // frame position of sequence b (a load)
+  __device__ __forceinline__ int pos(const AttnArgs& a, int b) const { return a.frame_pos[b]; }
   // the last b in [0, B) with pre(b) * hkv <= x (uniform)
   __device__ __forceinline__ int last_at_or_below(int B, int hkv, int64_t x) const {
     int lo_i = 0, hi_i = B - 1;
@@ -705,8 +707,12 @@ struct PreLds {
 struct PreReg {
   int v;
   int total;
+  int p;  // lane b: frame position of sequence b, as loaded for the prefix
   __device__ __forceinline__ int operator()(int i) const {
     return i < kWave ? __builtin_amdgcn_readlane(v, i) : total;
+  }
+  __device__ __forceinline__ int pos(const AttnArgs&, int b) const {
+    return __builtin_amdgcn_readlane(p, b);
   }
   __device__ __forceinline__ int last_at_or_below(int B, int hkv, int64_t x) const {
     // pre is non-decreasing, so the lanes that qualify are a prefix of [0, B)
@@ -789,10 +795,11 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const Pre& s_pr
     const int pre_b = __builtin_amdgcn_readfirstlane(s_pre(b));
     const int seg = static_cast<int>(min(static_cast<int64_t>(n - j), wend - cur));
     const int64_t item_beg = static_cast<int64_t>(pre_b) * a.Hkv + static_cast<int64_t>(h) * n;
-    // The item's frame position, its first table window and its queries are
-    // loaded together.  Without a window the keys start at 0, so the first
-    // sub-tile (j) and its table window do not depend on the position.
-    const int fp_raw = a.frame_pos[b];
+    // The item's frame position (from the prefix's registers when it has
+    // them), its first table window and its queries are loaded together.
+    // Without a window the keys start at 0, so the first sub-tile (j) and its
+    // table window do not depend on the position.
+    const int fp_raw = s_pre.pos(a, b);
     Item<BK, WINDOWED, KP> it(a, b, h);
     // without a window: the window must hold column jr*kSub/BK; only an item
     // shorter than a share can carry a start cost (jr = j - kItemCost)
@@ -859,6 +866,34 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const Pre& s_pr
     }
     if (WINDOWED) it.load_window(it.clampc(((lo / kSub + jr) * kSub) / BK));
 
+    const int t0 = lo / kSub + jr;
+    const int tlast = t0 + segr - 1;
+    // Two-stage software pipeline over the segment's sub-tiles, run per
+    // window of kWinEntries table entries.
+    // The first run of a segment is shortened by a per-wave amount so that the
+    // waves of a workgroup reach their run boundaries (where the ring drains
+    // and refills) at different times and cover each other's bubbles.
+    int span = __builtin_amdgcn_readfirstlane(kWinEntries - 16 * ((threadIdx.x >> 6) & 3));
+    int tw = t0, twl = t0;
+    // Ring of kDepth slots: sub-tile k lives in slot (k - tw) % kDepth.  While
+    // sub-tile k is computed from registers, sub-tile k+1 is read from its
+    // slot into the other register stage and up to kDepth-1 later sub-tiles
+    // are in flight; slot k is refilled once k has been consumed.
+    static_assert(kDepth % 2 == 0, "register stages alternate with the slot index");
+    auto start_run = [&]() {
+      const int cw0 = it.clampc((tw * kSub) / BK);
+      if (cw0 < it.tab_base || cw0 >= it.tab_base + kWinEntries) it.load_window(cw0);
+      const int cend = min(it.tab_base + kWinEntries, cw0 + span);  // first column past the run
+      twl = max(tw, min(tlast, (cend * BK) / kSub - 1));
+      span = kWinEntries;
+#pragma unroll
+      for (int d = 0; d < kDepth; ++d)
+        if (tw + d <= twl) it.issue(ring, d, tw + d);
+    };
+    // the first run's K/V loads go out before anything waits for the queries
+    // or the new token's rows, so those loads overlap the ring fill
+    start_run();
+
     if (rope) rotate_queries(q0, q1, rc, rs, q >= 2);
     // expanded queries: qx[i][k] holds q[g][16q + 4i + k] in the half of parity e
     uint32_t qx[4][4];
@@ -894,29 +929,9 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const Pre& s_pr
     for (int t = 0; t < 4; ++t) s.acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     s.m = -INFINITY;
     s.l = 0.f;
-    const int t0 = lo / kSub + jr;
-    const int tlast = t0 + segr - 1;
 
-    // Two-stage software pipeline over the segment's sub-tiles, run per
-    // window of kWinEntries table entries.
-    // The first run of a segment is shortened by a per-wave amount so that the
-    // waves of a workgroup reach their run boundaries (where the ring drains
-    // and refills) at different times and cover each other's bubbles.
-    int span = __builtin_amdgcn_readfirstlane(kWinEntries - 16 * ((threadIdx.x >> 6) & 3));
-    for (int tw = t0; tw <= tlast;) {
-      const int cw0 = it.clampc((tw * kSub) / BK);
-      if (cw0 < it.tab_base || cw0 >= it.tab_base + kWinEntries) it.load_window(cw0);
-      const int cend = min(it.tab_base + kWinEntries, cw0 + span);  // first column past the run
-      const int twl = max(tw, min(tlast, (cend * BK) / kSub - 1));
-      span = kWinEntries;
-      // Ring of kDepth slots: sub-tile k lives in slot (k - tw) % kDepth.  While
-      // sub-tile k is computed from registers, sub-tile k+1 is read from its
-      // slot into the other register stage and up to kDepth-1 later sub-tiles
-      // are in flight; slot k is refilled once k has been consumed.
-      static_assert(kDepth % 2 == 0, "register stages alternate with the slot index");
-#pragma unroll
-      for (int d = 0; d < kDepth; ++d)
-        if (tw + d <= twl) it.issue(ring, d, tw + d);
+    for (bool first = true; tw <= tlast; first = false) {
+      if (!first) start_run();
       Stage st[2];
       wait_vmcnt_slots(min(twl - tw, kDepth - 1));
       if (tw == t_new) write_new_token(it, ring, 0, hi, kcode, vcode);
@@ -1093,11 +1108,12 @@ __global__ void __launch_bounds__(kThreads, kWGPerCU * kWavesPerWG / 4) decode_a
     // Every wave scans the (at most 64) positions in registers: no LDS, no
     // barrier between the position load and the wave's first item.
     const int lane = tid & (kWave - 1);
-    int n = 0;
+    int n = 0, posv = 0;
     if (lane < B) {
       int lo = 0;
       bool inv;
-      n = seq_subtiles<BK, WINDOWED>(a, a.frame_pos[lane], &lo, &inv);
+      posv = a.frame_pos[lane];
+      n = seq_subtiles<BK, WINDOWED>(a, posv, &lo, &inv);
     }
     int x = n;  // inclusive prefix over the lanes
 #pragma unroll
@@ -1140,7 +1156,7 @@ __global__ void __launch_bounds__(kThreads, kWGPerCU * kWavesPerWG / 4) decode_a
         if (lane >= off) xv += y;
       }
     }
-    const PreReg pre{xv - v, __builtin_amdgcn_readlane(xv, kWave - 1)};
+    const PreReg pre{xv - v, __builtin_amdgcn_readlane(xv, kWave - 1), posv};
     run_shares<BK, WINDOWED, KP, ROPE>(a, pre, B, longest, ring, wg, per_r, half);
   } else {
     if (tid == 0) {
