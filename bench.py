@@ -196,7 +196,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              f"(the decode step is data-parallel over sequences and KV heads, see DESIGN.md)",
+              f"(the decode step is data-parallel over sequences and KV heads: each GPU would "
+              f"run this step on its own share)",
               file=sys.stderr)
         sys.exit(2)
 
