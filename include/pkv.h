@@ -66,13 +66,11 @@ int pkv_abi_version(void);
 const char* pkv_last_error(void);
 
 /* Host only.  Bytes the KV cache may take on a device ("determine_available_
- * memory design", "Heuristic formula", "Minimum KV guard" and the shared budget
- * logic of "How this is implemented"):
- *   total_budget = int(total_hbm_bytes * gmu)
- *   available    = max(min(max(total_budget - bytes_used, 0),
- *                          int(total_budget * cap_fraction)), 0)
- * with int() truncating toward zero and doubles as in Python (the page's
- * defaults: cap_fraction 0.30, min_kv_gib 1.0).  *available_bytes (host) is
+ * memory design": "How GMU works", "Heuristic formula", "Minimum KV guard").
+ * The engine's share of the device is int(total_hbm_bytes * gmu); the cache
+ * gets that share less bytes_used, clamped into [0, int(share * cap_fraction)]
+ * (int() truncating toward zero, doubles as in Python; the page's defaults
+ * are cap_fraction 0.30 and min_kv_gib 1.0).  *available_bytes (host) is
  * written in every non-ARG case; a budget below min_kv_gib GiB returns
  * PKV_ERR_DATA.  Byte counts must lie in [0, 2^52], gmu and cap_fraction in
  * [0, 1]. */

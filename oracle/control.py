@@ -21,17 +21,28 @@ Readings (design notes):
   * an update index is the cache slot ``block_id * Bk + offset`` (int64);
     inactive sequences get -1 everywhere (no write, no read, zero output), and
     so does an update index whose table entry is negative (no block).
+  * "DI wiring (NIXL)" (sliding-window DI truncation): a decode node that
+    admits a prompt of N tokens but recomputes its last token would evict the
+    window's oldest block one step early at ``N % block_size ==
+    block_size - 1``; the fix makes both nodes operate at N - 1.  Reading
+    taken for the setup: an optional lag of one token in the window frame's
+    anchor.  With ``anchor_lag = 1`` the frame's first block is the one the
+    step at ``p - 1`` would use, ``f = max(0, p - 1 - W + 1) // Bk``, so the
+    oldest block stays in the trimmed table one step longer (it leaves at
+    ``p % Bk == 0`` instead of ``p % Bk == Bk - 1``).  The attended keys stay
+    ``[p - W + 1, p]``; the trimmed table is
+    ``ceil((W - 1 + anchor_lag) / Bk) + 1`` wide.
 """
 import numpy as np
 
 
-def trimmed_width(window: int, block: int) -> int:
-    """Most logical blocks a ``window``-token span can touch."""
-    return -(-(window - 1) // block) + 1
+def trimmed_width(window: int, block: int, anchor_lag: int = 0) -> int:
+    """Most logical blocks a frame of ``window + anchor_lag`` tokens can touch."""
+    return -(-(window - 1 + anchor_lag) // block) + 1
 
 
 def attention_control(seq_lens, active, bt_full, bt_swa, block: int, window: int,
-                      positions=None):
+                      positions=None, anchor_lag: int = 0):
     """Return the per-step control as a dict of numpy arrays.
 
     bt_full, bt_swa : int32 [B, width] tables indexed by logical block.
@@ -39,10 +50,13 @@ def attention_control(seq_lens, active, bt_full, bt_swa, block: int, window: int
     position), ``bt_swa_trim`` (int32 [B, n_swa]), ``upd_full`` and
     ``upd_swa`` (int64 [B] cache slots), ``pos_abs`` (int64 [B], the absolute
     positions carried for the rotary stage; -1 when not given or inactive).
+    anchor_lag : 0, or 1 for the N - 1 reading of "DI wiring (NIXL)" above.
     """
+    if anchor_lag not in (0, 1):
+        raise ValueError("anchor_lag must be 0 or 1")
     seq_lens = np.asarray(seq_lens)
     B = seq_lens.shape[0]
-    n_swa = trimmed_width(window, block)
+    n_swa = trimmed_width(window, block, anchor_lag)
     pos_full = np.full(B, -1, dtype=np.int32)
     pos_swa = np.full(B, -1, dtype=np.int32)
     trim = np.full((B, n_swa), -1, dtype=np.int32)
@@ -56,7 +70,7 @@ def attention_control(seq_lens, active, bt_full, bt_swa, block: int, window: int
         pos_full[b] = p
         blk_full = int(bt_full[b, p // block])
         upd_full[b] = blk_full * block + p % block if blk_full >= 0 else -1
-        first = max(0, p - window + 1) // block
+        first = max(0, p - anchor_lag - window + 1) // block
         for c in range(first, p // block + 1):
             trim[b, c - first] = bt_swa[b, c]
         wf = p - first * block

@@ -85,11 +85,12 @@ int pkv_kv_budget(int64_t total_hbm_bytes, int64_t bytes_used, double gmu, doubl
   if (!(gmu >= 0.0 && gmu <= 1.0) || !(cap_fraction >= 0.0 && cap_fraction <= 1.0) ||
       !(min_kv_gib >= 0.0 && min_kv_gib < 1e9))
     return fail(PKV_ERR_ARG, "gmu and cap_fraction must be in [0, 1], min_kv_gib >= 0");
-  // int(x) of a double truncates toward zero; byte counts below 2^53 convert exactly
-  const int64_t total_budget = static_cast<int64_t>(static_cast<double>(total_hbm_bytes) * gmu);
-  const int64_t user_budget = std::max<int64_t>(total_budget - bytes_used, 0);
-  const int64_t cap = static_cast<int64_t>(static_cast<double>(total_budget) * cap_fraction);
-  const int64_t available = std::max<int64_t>(std::min(user_budget, cap), 0);
+  // The engine's share of the device, and the resident bytes taken out of
+  // it, clamped into [0, cap * share].  int(x) of a double truncates toward
+  // zero; byte counts below 2^53 convert exactly.
+  const int64_t share = static_cast<int64_t>(static_cast<double>(total_hbm_bytes) * gmu);
+  const int64_t cap = static_cast<int64_t>(static_cast<double>(share) * cap_fraction);
+  const int64_t available = std::clamp<int64_t>(share - bytes_used, 0, cap);
   *available_bytes = available;
   if (static_cast<double>(available) < min_kv_gib * 1073741824.0)
     return fail(PKV_ERR_DATA, "KV budget of %lld bytes is below the minimum of %g GiB",

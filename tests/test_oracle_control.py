@@ -119,3 +119,86 @@ def test_csr_hand_example():
     assert sl.tolist() == [10, 4]
     assert f.tolist() == [[7, 2, 9, -1, -1], [5, -1, -1, -1, -1]]
     assert s.tolist() == [[-1, 11, 12, -1, -1], [13, -1, -1, -1, -1]]
+
+
+def _run_lag(block, lag, n_tok=3000):
+    p = np.arange(n_tok)
+    B = p.size
+    width = -(-n_tok // block) + 1
+    bt_full = np.tile(np.arange(width, dtype=np.int32) + 10_000, (B, 1))
+    bt_swa = np.tile(np.arange(width, dtype=np.int32) + 50_000, (B, 1))
+    ctl = C.attention_control(p + 1, np.ones(B, np.uint8), bt_full, bt_swa, block, W,
+                              anchor_lag=lag)
+    return p, bt_swa, ctl
+
+
+@pytest.mark.parametrize("block", [16, 32, 128])
+def test_lagged_anchor_keeps_the_oldest_block_one_step_longer(block):
+    """"DI wiring (NIXL)": with the frame anchored one token back (both nodes
+    at N - 1) the oldest block is not dropped at the printed boundary
+    N % block_size == block_size - 1 but one step later, and the frame of
+    step p is exactly the frame the unlagged setup gives step p - 1."""
+    g = json.load(open(os.path.join(GOLD, "swa_eviction_boundary.json")))
+    assert g["window"] == W and block in g["block_sizes"]
+    p, bt_swa, lag = _run_lag(block, 1)
+    _, _, ref = _run_lag(block, 0)
+    assert C.trimmed_width(W, block, 1) == C.trimmed_width(W, block) == lag["bt_swa_trim"].shape[1]
+    first = lag["bt_swa_trim"][:, 0]
+    for b in range(1, p.size):
+        pb = int(p[b])
+        advanced = first[b] != first[b - 1]
+        assert advanced == (pb % block == 0 and pb >= W + block), pb
+        if pb % block == block - 1 and pb >= W:
+            # the printed boundary: the unlagged frame just dropped a block,
+            # the lagged one still holds it (the block of token p - W)
+            assert ref["bt_swa_trim"][b, 0] != ref["bt_swa_trim"][b - 1, 0]
+            assert first[b] == ref["bt_swa_trim"][b - 1, 0] == bt_swa[b, (pb - W) // block]
+        # frame of p with the lag == frame of p - 1 without it
+        origin_lag = pb - int(lag["pos_swa"][b])
+        origin_ref = (pb - 1) - int(ref["pos_swa"][b - 1])
+        assert origin_lag == origin_ref
+        # the window's keys are all still in the lagged frame, and the
+        # write index is the same slot
+        trim = lag["bt_swa_trim"][b]
+        for t in range(max(0, pb - W + 1), pb + 1):
+            assert trim[(t - origin_lag) // block] == bt_swa[b, t // block]
+        assert lag["upd_swa"][b] == ref["upd_swa"][b]
+        assert lag["pos_full"][b] == ref["pos_full"][b] and lag["upd_full"][b] == ref["upd_full"][b]
+
+
+def test_lagged_trimmed_width_grows_only_when_needed():
+    # a window of 17 keys at block 16 spans 2 blocks, plus one lagged token 3
+    assert C.trimmed_width(17, 16, 0) == 2 and C.trimmed_width(17, 16, 1) == 3
+    assert [C.trimmed_width(W, b, 1) for b in (16, 32, 128)] == [9, 5, 2]
+    with pytest.raises(ValueError):
+        C.attention_control([5], [1], np.zeros((1, 1), np.int32), np.zeros((1, 1), np.int32),
+                            16, W, anchor_lag=2)
+
+
+@pytest.mark.parametrize("block", [16, 32])
+def test_lagged_frame_attends_the_same_keys(block):
+    """Window attention through the lagged frame equals attention through the
+    unlagged one exactly (same keys, same order), at every offset around two
+    eviction boundaries."""
+    from oracle import attention as OA
+    from paged_build import bf16_values, random_codes
+    rng = np.random.default_rng(block)
+    H, D = 1, 64
+    lens = np.arange(W + block - 3, W + 2 * block + 3)      # p across two boundaries
+    B = lens.size
+    width = -(-int(lens.max()) // block)
+    nb = width * B + 4
+    perm = rng.permutation(nb)
+    bt_swa = perm[:B * width].reshape(B, width).astype(np.int32)
+    bt_full = np.full_like(bt_swa, -1)
+    half = nb * H * block * D
+    kh = random_codes(rng, (half,))
+    vh = random_codes(rng, (half,))
+    q = bf16_values(rng, (B, 2, D))
+    outs = []
+    for lag in (0, 1):
+        ctl = C.attention_control(lens, np.ones(B, np.uint8), bt_swa, bt_swa, block, W,
+                                  anchor_lag=lag)
+        outs.append(OA.paged_decode_attention(q, kh, vh, ctl["bt_swa_trim"], ctl["pos_swa"], W,
+                                              block, H, 0.125, 0.0625, 0.125))
+    assert np.array_equal(outs[0], outs[1])
