@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 2
+#define PKV_ABI_VERSION 3
 
 typedef enum {
   PKV_OK = 0,
@@ -91,8 +91,9 @@ int pkv_kv_buffer_bytes(int64_t num_blocks, int32_t kv_heads, int32_t block,
                         int32_t head_dim, int64_t* half_bytes, int64_t* total_bytes);
 
 /* Host only.  Width of the trimmed sliding-window table: the most logical
- * blocks a window of `window` tokens can touch, ceil((window-1)/block) + 1. */
-int pkv_trimmed_width(int32_t window, int32_t block);
+ * blocks the window frame can touch, ceil((window-1+anchor_lag)/block) + 1
+ * (anchor_lag 0 or 1, as in pkv_setup_attn_control). */
+int pkv_trimmed_width(int32_t window, int32_t block, int32_t anchor_lag);
 
 /* Layer-invariant attention control, built once per step ("Kernel contract").
  *
@@ -102,10 +103,16 @@ int pkv_trimmed_width(int32_t window, int32_t block);
  * bt_full / bt_swa int32 [batch, *] tables indexed by logical block with row
  * strides bt_full_stride / bt_swa_stride (elements) and `bt_width` valid
  * columns each.
+ * anchor_lag (host, 0 or 1): 1 anchors the window frame one token back, at
+ * p - 1, so that the window's oldest block stays in the trimmed table one
+ * step past the boundary p % block == block-1 -- the reading taken here of
+ * the sliding-window DI truncation of "DI wiring (NIXL)" (both nodes operate
+ * at N-1).  The attended keys do not change.
  * Outputs (device): pos_full int32 [batch] = p; pos_swa int32 [batch] = the
- * window-frame position p - f*block with f = max(0, p-window+1)/block;
+ * window-frame position p - f*block with
+ * f = max(0, p-anchor_lag-window+1)/block;
  * bt_swa_trim int32 [batch, trim_width] = bt_swa[b, f .. p/block] padded with
- * -1 (trim_width must equal pkv_trimmed_width(window, block));
+ * -1 (trim_width must equal pkv_trimmed_width(window, block, anchor_lag));
  * upd_full / upd_swa int64 [batch] = cache slots block_id*block + offset of
  * the new token in the full / sliding-window table; pos_abs int64 [batch]
  * (may be NULL) = positions, carried for the rotary stage.
@@ -113,7 +120,7 @@ int pkv_trimmed_width(int32_t window, int32_t block);
  * beyond bt_width keeps pos_full = p (so attention reports it as NaN) but gets
  * update slots of -1.  A table entry < 0 at the new token gives slot -1. */
 int pkv_setup_attn_control(int32_t batch, int32_t block, int32_t window,
-                           const int32_t* seq_lens, const uint8_t* active,
+                           int32_t anchor_lag, const int32_t* seq_lens, const uint8_t* active,
                            const int64_t* positions,
                            const int32_t* bt_full, int32_t bt_full_stride,
                            const int32_t* bt_swa, int32_t bt_swa_stride, int32_t bt_width,
@@ -136,7 +143,8 @@ int pkv_setup_attn_control(int32_t batch, int32_t block, int32_t window,
  * pkv_paged_decode_attn / pkv_step.  All arrays are device arrays; kv_indptr
  * has batch+1 entries and must be non-decreasing (not checked here). */
 int pkv_setup_attn_control_csr(int32_t batch, int32_t block, int32_t window,
-                               const int32_t* kv_indptr, const int32_t* full_indices,
+                               int32_t anchor_lag, const int32_t* kv_indptr,
+                               const int32_t* full_indices,
                                const int32_t* swa_indices, const int32_t* last_page_len,
                                const uint8_t* active, const int64_t* positions, int32_t* bt_full,
                                int32_t bt_stride, int32_t bt_width, int32_t* seq_lens,
@@ -213,8 +221,8 @@ int pkv_paged_decode_attn(int32_t batch, int32_t q_heads, int32_t kv_heads, int3
  * control produced by pkv_setup_attn_control.  Host struct; the pointer
  * members are device pointers except the two buffer arrays, which are host
  * arrays of n_buffers device pointers.  Exactly one KV form must be given:
- * the per-buffer form (k_bufs/v_bufs) or the stacked form (k_stacked/v_stacked:
- * one allocation of n_buffers consecutive shared buffers, K half then V half
+ * the per-buffer form (k_bufs/v_bufs) or the stacked form (`stacked`: one
+ * allocation of n_buffers consecutive shared buffers, K half then V half
  * each) -- "Kernel contract". */
 typedef struct pkv_step {
   int32_t batch, q_heads, kv_heads, head_dim, block, window;
@@ -237,22 +245,24 @@ typedef struct pkv_step {
 } pkv_step;
 
 /* One layer of the alternating schedule ("Kernel contract"): layer i writes
- * its new K/V into buffer i/2 and attends with the trimmed table,
- * window-frame positions and window `step->window` (i even) or the full
- * table, p and no window (i odd).  Shapes as in pkv_kv_cache_update /
- * pkv_paged_decode_attn.
+ * its new K/V into buffer i/2 through update index upd_swa (i even) or
+ * upd_full (i odd) and attends with the trimmed table, window-frame
+ * positions and window `step->window` (i even) or the full table, p and no
+ * window (i odd).  Shapes as in pkv_kv_cache_update / pkv_paged_decode_attn.
  *
  * Both happen in one launch: the attention quantises each active sequence's
- * new token (code = E4M3(fp32(x) / fp32(scale))), stores it in the slot the
- * layer's table gives for the sequence's frame position -- the slot
- * upd_swa / upd_full name when the control comes from pkv_setup_attn_control,
- * which is this entry point's precondition -- and attends to it.  Buffer
- * bytes and outputs are identical to pkv_kv_cache_update followed by
+ * new token (code = E4M3(fp32(x) / fp32(scale))), stores it through the
+ * layer's update index and attends to it.  Buffer bytes and outputs are
+ * identical to pkv_kv_cache_update with that index followed by
  * pkv_paged_decode_attn (with the step's rope_cos / rope_sin passed to both
  * when given: the new K is turned before it is quantised, every query head
- * before the scores).  No id outside [0, num_blocks) is written.  The
- * block holding a sequence's new token must not appear in another sequence's
- * table of the same layer (its old bytes could be read there). */
+ * before the scores) whenever each update index is -1 (no write: the
+ * attention reads the cache as it is) or the slot the layer's table gives for
+ * the sequence's frame position, as pkv_setup_attn_control produces.  Any
+ * other index makes that sequence's output row NaN and writes nothing for
+ * it.  No id outside [0, num_blocks) is written.  The block holding a
+ * sequence's new token must not appear in another sequence's table of the
+ * same layer (its old bytes could be read there). */
 int pkv_decode_layer(const pkv_step* step, int32_t layer, const uint16_t* q,
                      const uint16_t* k_new, const uint16_t* v_new, float k_scale,
                      float v_scale, float sm_scale, uint16_t* out, void* workspace,

@@ -16,7 +16,7 @@ from . import attention, control, update
 def decode_step(buffers, q, k_new, v_new, seq_lens, active, bt_full, bt_swa,
                 block: int, kv_heads: int, window: int, k_scale, v_scale,
                 sm_scale: float, k_packed: bool = True, layers=None, kinds=None,
-                rope_cos=None, rope_sin=None):
+                rope_cos=None, rope_sin=None, anchor_lag: int = 0):
     """Run ``len(q)`` layers in place on ``buffers``.
 
     buffers : list of (k_half, v_half) flat uint8 arrays, one pair per buffer.
@@ -28,9 +28,13 @@ def decode_step(buffers, q, k_new, v_new, seq_lens, active, bt_full, bt_swa,
               alternating schedule (even layers sliding-window).
     rope_cos, rope_sin : optional float32 [B, D/2]; the one rotation of this
               step's queries and new keys, shared by every layer.
+    anchor_lag : window-frame anchor lag of the control (``control``, the
+              N - 1 reading of "DI wiring (NIXL)"); the attended keys are the
+              same either way.
     Returns (outputs dict layer -> [B, Hq, D] float64, control dict).
     """
-    ctl = control.attention_control(seq_lens, active, bt_full, bt_swa, block, window)
+    ctl = control.attention_control(seq_lens, active, bt_full, bt_swa, block, window,
+                                    anchor_lag=anchor_lag)
     outs = {}
     for i in range(len(q)):
         k_half, v_half = buffers[i // 2]

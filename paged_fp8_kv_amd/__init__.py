@@ -48,14 +48,15 @@ _SIGS = {
     "pkv_abi_version": ([], _i32),
     "pkv_last_error": ([], ctypes.c_char_p),
     "pkv_kv_buffer_bytes": ([_i64, _i32, _i32, _i32, ctypes.POINTER(_i64), ctypes.POINTER(_i64)], _i32),
-    "pkv_trimmed_width": ([_i32, _i32], _i32),
+    "pkv_trimmed_width": ([_i32, _i32, _i32], _i32),
     "pkv_kv_budget": ([_i64, _i64, ctypes.c_double, ctypes.c_double, ctypes.c_double,
                        ctypes.POINTER(_i64)], _i32),
     "pkv_kv_num_blocks": ([_i64, _i32, _i32, _i32, _i32, ctypes.POINTER(_i64)], _i32),
-    "pkv_setup_attn_control": ([_i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
-                                _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp], _i32),
-    "pkv_setup_attn_control_csr": ([_i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
-                                    _i32, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp], _i32),
+    "pkv_setup_attn_control": ([_i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32,
+                                _i32, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp], _i32),
+    "pkv_setup_attn_control_csr": ([_i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                    _i32, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp],
+                                   _i32),
     "pkv_kv_cache_update": ([_i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _i32, _vp, _vp,
                              _vp, _vp, _f32, _f32, _vp], _i32),
     "pkv_decode_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32, _i32, _i32], _i64),
@@ -69,7 +70,7 @@ _SIGS = {
 }
 
 _lib = None
-ABI_VERSION = 2  # PKV_ABI_VERSION these signatures follow
+ABI_VERSION = 3  # PKV_ABI_VERSION these signatures follow
 
 
 def lib():
@@ -144,16 +145,16 @@ def pkv_kv_num_blocks(available_bytes, n_buffers, kv_heads, block, head_dim):
     return out.value
 
 
-def pkv_trimmed_width(window, block):
-    return _check(lib().pkv_trimmed_width(window, block))
+def pkv_trimmed_width(window, block, anchor_lag=0):
+    return _check(lib().pkv_trimmed_width(window, block, anchor_lag))
 
 
 def pkv_setup_attn_control(seq_lens, active, bt_full, bt_swa, block, window, positions=None,
-                           bt_width=None, out=None, stream=None):
+                           bt_width=None, out=None, stream=None, anchor_lag=0):
     """Returns a dict with pos_full, pos_swa, bt_swa_trim, upd_full, upd_swa, pos_abs."""
     B = seq_lens.shape[0]
     width = bt_full.shape[1] if bt_width is None else bt_width
-    tw = pkv_trimmed_width(window, block) if window > 0 else 0
+    tw = pkv_trimmed_width(window, block, anchor_lag) if window > 0 else 0
     dev = seq_lens.device
     if out is None:
         out = dict(
@@ -165,7 +166,7 @@ def pkv_setup_attn_control(seq_lens, active, bt_full, bt_swa, block, window, pos
             pos_abs=torch.empty(B, dtype=torch.int64, device=dev),
         )
     _check(lib().pkv_setup_attn_control(
-        B, block, window, _dev_ptr(seq_lens, torch.int32, "seq_lens"),
+        B, block, window, anchor_lag, _dev_ptr(seq_lens, torch.int32, "seq_lens"),
         _dev_ptr(active, torch.uint8, "active"), _dev_ptr(positions, torch.int64, "positions"),
         _dev_ptr(bt_full, torch.int32, "bt_full"), bt_full.shape[1],
         _dev_ptr(bt_swa, torch.int32, "bt_swa") if window > 0 else None,
@@ -189,12 +190,13 @@ def _halves(buf, num_blocks, kv_heads, block, head_dim):
 
 
 def pkv_setup_attn_control_csr(kv_indptr, full_indices, swa_indices, last_page_len, active,
-                               block, window, bt_width, positions=None, out=None, stream=None):
+                               block, window, bt_width, positions=None, out=None, stream=None,
+                               anchor_lag=0):
     """Control from compressed page lists.  Returns the dict of
     pkv_setup_attn_control plus seq_lens and the padded full table bt_full
     (written into `out` when given, e.g. for graph capture)."""
     B = kv_indptr.shape[0] - 1
-    tw = pkv_trimmed_width(window, block) if window > 0 else 0
+    tw = pkv_trimmed_width(window, block, anchor_lag) if window > 0 else 0
     dev = kv_indptr.device
     if out is None:
         out = dict(
@@ -208,7 +210,7 @@ def pkv_setup_attn_control_csr(kv_indptr, full_indices, swa_indices, last_page_l
             pos_abs=torch.empty(B, dtype=torch.int64, device=dev),
         )
     _check(lib().pkv_setup_attn_control_csr(
-        B, block, window, _dev_ptr(kv_indptr, torch.int32, "kv_indptr"),
+        B, block, window, anchor_lag, _dev_ptr(kv_indptr, torch.int32, "kv_indptr"),
         _dev_ptr(full_indices, torch.int32, "full_indices"),
         _dev_ptr(swa_indices, torch.int32, "swa_indices") if window > 0 else None,
         _dev_ptr(last_page_len, torch.int32, "last_page_len"),

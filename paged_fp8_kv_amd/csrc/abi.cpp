@@ -109,13 +109,16 @@ int pkv_kv_num_blocks(int64_t available_bytes, int32_t n_buffers, int32_t kv_hea
   return ok();
 }
 
-int pkv_trimmed_width(int32_t window, int32_t block) {
+int pkv_trimmed_width(int32_t window, int32_t block, int32_t anchor_lag) {
   if (window < 1 || block < 1) return fail(PKV_ERR_ARG, "window and block must be >= 1");
+  if (anchor_lag != 0 && anchor_lag != 1) return fail(PKV_ERR_ARG, "anchor_lag must be 0 or 1");
+  if (window > INT32_MAX / 2) return fail(PKV_ERR_ARG, "window too large");
   g_err.clear();
-  return (window - 1 + block - 1) / block + 1;
+  return (window - 1 + anchor_lag + block - 1) / block + 1;
 }
 
-int pkv_setup_attn_control(int32_t batch, int32_t block, int32_t window, const int32_t* seq_lens,
+int pkv_setup_attn_control(int32_t batch, int32_t block, int32_t window, int32_t anchor_lag,
+                           const int32_t* seq_lens,
                            const uint8_t* active, const int64_t* positions, const int32_t* bt_full,
                            int32_t bt_full_stride, const int32_t* bt_swa, int32_t bt_swa_stride,
                            int32_t bt_width, int32_t* pos_full, int32_t* pos_swa,
@@ -129,19 +132,22 @@ int pkv_setup_attn_control(int32_t batch, int32_t block, int32_t window, const i
     return fail(PKV_ERR_ARG, "need 1 <= bt_width <= bt_full_stride");
   if (!seq_lens || !active || !bt_full || !pos_full || !upd_full)
     return fail(PKV_ERR_ARG, "null device pointer");
+  if (anchor_lag != 0 && anchor_lag != 1) return fail(PKV_ERR_ARG, "anchor_lag must be 0 or 1");
   if (window > 0) {
     if (!bt_swa || !pos_swa || !bt_swa_trim || !upd_swa)
       return fail(PKV_ERR_ARG, "window > 0 needs bt_swa, pos_swa, bt_swa_trim and upd_swa");
     if (bt_swa_stride < bt_width) return fail(PKV_ERR_ARG, "bt_swa_stride < bt_width");
-    const int need = (window - 1 + block - 1) / block + 1;
+    const int need = pkv_trimmed_width(window, block, anchor_lag);
+    if (need < 0) return need;
     if (trim_width != need)
-      return fail(PKV_ERR_ARG, "trim_width must be %d for window %d, block %d (got %d)", need,
-                  window, block, trim_width);
+      return fail(PKV_ERR_ARG, "trim_width must be %d for window %d, block %d, lag %d (got %d)",
+                  need, window, block, anchor_lag, trim_width);
   }
   pkv::SetupLaunch L{};
   L.B = batch;
   L.block = block;
   L.window = window;
+  L.anchor_lag = anchor_lag;
   L.seq_lens = seq_lens;
   L.active = active;
   L.positions = positions;
@@ -161,7 +167,7 @@ int pkv_setup_attn_control(int32_t batch, int32_t block, int32_t window, const i
 }
 
 int pkv_setup_attn_control_csr(int32_t batch, int32_t block, int32_t window,
-                               const int32_t* kv_indptr, const int32_t* full_indices,
+                               int32_t anchor_lag, const int32_t* kv_indptr, const int32_t* full_indices,
                                const int32_t* swa_indices, const int32_t* last_page_len,
                                const uint8_t* active, const int64_t* positions, int32_t* bt_full,
                                int32_t bt_stride, int32_t bt_width, int32_t* seq_lens,
@@ -177,18 +183,21 @@ int pkv_setup_attn_control_csr(int32_t batch, int32_t block, int32_t window,
   if (!kv_indptr || !full_indices || !last_page_len || !active || !bt_full || !seq_lens ||
       !pos_full || !upd_full)
     return fail(PKV_ERR_ARG, "null device pointer");
+  if (anchor_lag != 0 && anchor_lag != 1) return fail(PKV_ERR_ARG, "anchor_lag must be 0 or 1");
   if (window > 0) {
     if (!swa_indices || !pos_swa || !bt_swa_trim || !upd_swa)
       return fail(PKV_ERR_ARG, "window > 0 needs swa_indices, pos_swa, bt_swa_trim and upd_swa");
-    const int need = (window - 1 + block - 1) / block + 1;
+    const int need = pkv_trimmed_width(window, block, anchor_lag);
+    if (need < 0) return need;
     if (trim_width != need)
-      return fail(PKV_ERR_ARG, "trim_width must be %d for window %d, block %d (got %d)", need,
-                  window, block, trim_width);
+      return fail(PKV_ERR_ARG, "trim_width must be %d for window %d, block %d, lag %d (got %d)",
+                  need, window, block, anchor_lag, trim_width);
   }
   pkv::SetupLaunch L{};
   L.B = batch;
   L.block = block;
   L.window = window;
+  L.anchor_lag = anchor_lag;
   L.active = active;
   L.positions = positions;
   L.bt_full_stride = bt_stride;
@@ -271,7 +280,7 @@ static int attn_impl(int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t h
                      const int32_t* frame_pos, float k_scale, float v_scale, float sm_scale,
                      uint16_t* out, void* workspace, int64_t workspace_bytes, void* stream,
                      const uint16_t* k_new, const uint16_t* v_new, uint8_t* k_w, uint8_t* v_w,
-                     const float* rope_cos, const float* rope_sin) {
+                     const int64_t* upd, const float* rope_cos, const float* rope_sin) {
   if (batch < 0) return fail(PKV_ERR_ARG, "batch must be >= 0");
   if (batch == 0) return ok();
   if (batch > pkv::kMaxBatch)
@@ -341,6 +350,7 @@ static int attn_impl(int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t h
   L.v_new = v_new;
   L.k_w = k_w;
   L.v_w = v_w;
+  L.upd = upd;
   L.rope_cos = rope_cos;
   L.rope_sin = rope_sin;
   return hip_status(pkv::launch_decode_attn(L, static_cast<hipStream_t>(stream)), "attention launch");
@@ -356,7 +366,7 @@ int pkv_paged_decode_attn(int32_t batch, int32_t q_heads, int32_t kv_heads, int3
   return attn_impl(batch, q_heads, kv_heads, head_dim, block, num_blocks, window, q, k_half,
                    k_packed, v_half, block_table, bt_stride, table_width, frame_pos, k_scale,
                    v_scale, sm_scale, out, workspace, workspace_bytes, stream, nullptr, nullptr,
-                   nullptr, nullptr, rope_cos, rope_sin);
+                   nullptr, nullptr, nullptr, rope_cos, rope_sin);
 }
 
 int pkv_decode_layer(const pkv_step* s, int32_t layer, const uint16_t* q, const uint16_t* k_new,
@@ -385,21 +395,23 @@ int pkv_decode_layer(const pkv_step* s, int32_t layer, const uint16_t* q, const 
   }
   const bool swa = (layer % 2) == 0;
   if (swa && s->window < 1) return fail(PKV_ERR_ARG, "even layers need window >= 1");
-  // One launch: the attention writes each sequence's new token itself (into
-  // the slot its table gives for the frame position, which is the update
-  // index the setup call derived from the same table) and attends to it from
-  // registers.
+  // One launch: the attention writes each sequence's new token itself
+  // through the layer's update index (upd_swa / upd_full) and attends to it
+  // from registers.
   if (!k_new || !v_new) return fail(PKV_ERR_ARG, "null k_new / v_new");
   if (!aligned(k_new, 2) || !aligned(v_new, 2)) return fail(PKV_ERR_ARG, "k_new / v_new must be 2-byte aligned");
+  const int64_t* upd = swa ? s->upd_swa : s->upd_full;
+  if (!upd) return fail(PKV_ERR_ARG, "the step needs upd_swa and upd_full");
+  if (!aligned(upd, 8)) return fail(PKV_ERR_ARG, "update indices must be 8-byte aligned");
   if (swa)
     return attn_impl(s->batch, s->q_heads, s->kv_heads, s->head_dim, s->block, s->num_blocks,
                      s->window, q, kh, s->k_packed, vh, s->bt_swa_trim, s->trim_width,
                      s->trim_width, s->pos_swa, k_scale, v_scale, sm_scale, out, workspace,
-                     workspace_bytes, stream, k_new, v_new, kh, vh, s->rope_cos, s->rope_sin);
+                     workspace_bytes, stream, k_new, v_new, kh, vh, upd, s->rope_cos, s->rope_sin);
   return attn_impl(s->batch, s->q_heads, s->kv_heads, s->head_dim, s->block, s->num_blocks, 0, q,
                    kh, s->k_packed, vh, s->bt_full, s->bt_full_stride, s->bt_full_width,
                    s->pos_full, k_scale, v_scale, sm_scale, out, workspace, workspace_bytes, stream,
-                   k_new, v_new, kh, vh, s->rope_cos, s->rope_sin);
+                   k_new, v_new, kh, vh, upd, s->rope_cos, s->rope_sin);
 }
 
 int pkv_validate_attn_control(int32_t batch, int32_t block, int32_t window, int64_t num_blocks,

@@ -41,7 +41,9 @@ __device__ __forceinline__ void setup_one(const SetupLaunch& a, int b, int len, 
     a.upd_full[b] = blk >= 0 ? static_cast<int64_t>(blk) * BK + p % BK : -1;
   }
   if (a.window > 0) {
-    const int first = max(0, p - a.window + 1) / BK;
+    // anchor_lag 1 keeps the window's oldest block one step longer
+    // ("DI wiring (NIXL)": both nodes operate at N - 1)
+    const int first = max(0, p - a.anchor_lag - a.window + 1) / BK;
     for (int i = 0; i < a.trim_width; ++i) {
       const int c = first + i;
       trow[i] = (c <= cp && c < a.bt_width) ? swa(c) : -1;

@@ -92,6 +92,7 @@ struct AttnArgs {
   const uint16_t* v_new;
   uint8_t* k_w;
   uint8_t* v_w;
+  const int64_t* upd;  // write slot of each sequence's new token (-1: none)
   float k_scale;
   // rotary cos/sin fp32 [B, 32] (null: none) for the queries and the new K
   const float* rope_cos;
@@ -523,19 +524,23 @@ __device__ __forceinline__ void store_bf16x16(uint16_t* dst, const float* v) {
 }
 
 // Fused cache write of the new token at frame position hi of the item
-// (lane j: dim j): patch the slot holding its sub-tile, and store the codes
-// into the block the table gives for hi (skipped, like the separate update,
-// when that id is outside the pool -- the item is then flagged bad).
+// (lane j: dim j) through the sequence's update index `upd`: when it is the
+// slot the table gives for hi, patch the LDS slot holding the token's
+// sub-tile and store the codes there; when it is -1, write nothing and read
+// the cache as it is (as the separate update would); any other value, or a
+// table id outside the pool, flags the item bad (NaN row) and writes nothing.
 template <int BK, bool WINDOWED, bool KP>
 __device__ __forceinline__ void write_new_token(Item<BK, WINDOWED, KP>& it, uint8_t* ring, int slot,
-                                                int hi, uint32_t kcode, uint32_t vcode) {
-  patch_slot<KP>(ring, slot, hi % kSub, kcode, vcode);
+                                                int hi, int64_t upd, uint32_t kcode,
+                                                uint32_t vcode) {
+  if (upd < 0) return;
   const bool was_bad = it.bad;
   it.bad = false;
   const int blk = it.block_of(it.clampc(hi / BK));
-  const bool valid = !it.bad;
-  it.bad = was_bad || it.bad;
+  const bool valid = !it.bad && upd == static_cast<int64_t>(blk) * BK + hi % BK;
+  it.bad = was_bad || !valid;
   if (valid) {
+    patch_slot<KP>(ring, slot, hi % kSub, kcode, vcode);
     const int j = lane_id();
     const int tok = hi % BK;
     const int64_t tile = (static_cast<int64_t>(blk) * it.hkv + it.h) * (BK * kHeadDim);
@@ -828,10 +833,12 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const Pre& s_pr
     // only by the segment holding the token
     uint16_t kn_bits = 0, vn_bits = 0;
     float kn_c = 1.f, kn_s = 0.f;
+    int64_t upd_b = -1;
     if (a.k_new != nullptr) {
       const int64_t row = (static_cast<int64_t>(b) * a.Hkv + h) * kHeadDim + lane;
       kn_bits = a.k_new[row];
       vn_bits = a.v_new[row];
+      upd_b = a.upd[b];
       if (rope) {
         const int64_t ci = static_cast<int64_t>(b) * (kHeadDim / 2) + (lane & (kHeadDim / 2 - 1));
         kn_c = a.rope_cos[ci];
@@ -934,7 +941,7 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const Pre& s_pr
       if (!first) start_run();
       Stage st[2];
       wait_vmcnt_slots(min(twl - tw, kDepth - 1));
-      if (tw == t_new) write_new_token(it, ring, 0, hi, kcode, vcode);
+      if (tw == t_new) write_new_token(it, ring, 0, hi, upd_b, kcode, vcode);
       read_slot<KP>(ring, 0, st[0]);
       for (int i = tw; i <= twl; i += kDepth) {
 #pragma unroll
@@ -945,7 +952,8 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const Pre& s_pr
           // it (t32+2 .. min(twl, t32+kDepth-1)) are outstanding
           if (t32 < twl) {
             wait_vmcnt_slots(min(twl - t32 - 1, kDepth - 2));
-            if (t32 + 1 == t_new) write_new_token(it, ring, (d + 1) % kDepth, hi, kcode, vcode);
+            if (t32 + 1 == t_new)
+              write_new_token(it, ring, (d + 1) % kDepth, hi, upd_b, kcode, vcode);
             read_slot<KP>(ring, (d + 1) % kDepth, st[(d + 1) & 1]);
           }
           if (t32 * kSub >= lo && t32 * kSub + kSub - 1 <= hi)
@@ -1313,6 +1321,7 @@ hipError_t launch_decode_attn(const AttnLaunch& L, hipStream_t stream) {
   a.rope_sin = L.rope_sin;
   a.k_w = L.k_w;
   a.v_w = L.v_w;
+  a.upd = L.upd;
   a.n_workers = L.n_workers;
   a.partial_bytes = static_cast<int32_t>(static_cast<int64_t>(2) * L.n_workers * kSlotBytesF);
   // the workspace holds partial slots for at most this many workers

@@ -33,6 +33,10 @@ struct AttnLaunch {
   const uint16_t* v_new;
   uint8_t* k_w;
   uint8_t* v_w;
+  // Write slots of the fused write (int64 [B], block_id*block + offset): -1
+  // skips the write; any other value must be the slot the table gives for
+  // the frame position, else the row is NaN and nothing is written.
+  const int64_t* upd;
   // Optional rotary cos/sin, fp32 [B, 32] (null: no rotation): every query
   // head, and the new K before it is quantised, are turned half-split.
   const float* rope_cos;
@@ -46,6 +50,7 @@ hipError_t launch_decode_attn(const AttnLaunch& L, hipStream_t stream);
 
 struct SetupLaunch {
   int32_t B, block, window;
+  int32_t anchor_lag;  // 0, or 1: the window frame is anchored at p - 1
   const int32_t* seq_lens;
   const uint8_t* active;
   const int64_t* positions;

@@ -16,6 +16,27 @@ from oracle import step as OS
 from oracle import update as OU
 
 ATOL, RTOL = 2e-3, 1e-2
+# Tighter guards beside the tolerance above (what the kernel's arithmetic
+# allows, so that a small systematic error still fails):
+#  * element-wise: |gpu - ref| <= ULP_GUARD bf16 ulps of ref + FLOOR_GUARD.
+#    The output is rounded to bf16 once (half an ulp); before that the only
+#    error above fp32 rounding is the fp16 rounding of the softmax weights
+#    fed to the PV product (relative 2^-11 per weight), which matters only
+#    where the output nearly cancels -- hence the absolute floor;
+#  * aggregate: ||gpu - ref||_2 / ||ref||_2 <= L2_GUARD over all finite
+#    elements of a comparison.  bf16 rounding alone gives about 1.7e-3; a
+#    0.5% systematic error gives above 5e-3.
+# Measured on MI355X over every parity comparison (configs 1-5, all rows and
+# layers of the full sizes): at most 0.46 ulp beyond the floor, relative L2
+# 1.63e-3 .. 1.68e-3.
+ULP_GUARD, FLOOR_GUARD, L2_GUARD = 1.0, 2.0 ** -11, 2.5e-3
+# With rotary embedding the turned query is rounded to bf16 for the score
+# product (its float64 value in the oracle): scores move by about 1e-3, and
+# outputs by up to about 2.5e-3 absolute wherever the weights shift between
+# keys, so no element-wise bound tighter than the tolerance holds; the
+# aggregate guard stays (measured: relative L2 up to 2.7e-3).
+ROPE_GUARDS = dict(ulp_guard=None, l2_guard=4e-3)
+STATS = []   # (what, max abs err, max err in ulps beyond the floor, relative L2, max ulps)
 
 
 def alternating(cfg):
@@ -72,24 +93,54 @@ def device_inputs(wl, dev):
                 v_new=wl.v_new.to(dev))
 
 
-def gpu_step(wl, bufs, dev, use_layer_api=True, workspaces=None, k_packed=True, rope=None):
+def csr_lists(wl):
+    """The workload's padded tables as compressed page lists (plain loops):
+    (kv_indptr, full_indices, swa_indices, last_page_len) int32 arrays."""
+    Bk = wl.cfg.block
+    indptr, full, swa, last = [0], [], [], []
+    for b in range(wl.cfg.batch):
+        n = -(-int(wl.seq_lens[b]) // Bk)
+        full += [int(x) for x in wl.bt_full[b, :n]]
+        swa += [int(x) for x in wl.bt_swa[b, :n]]
+        indptr.append(indptr[-1] + n)
+        last.append(int(wl.seq_lens[b]) - (n - 1) * Bk if n else 0)
+    a = lambda x: np.asarray(x, dtype=np.int32)
+    return a(indptr), a(full), a(swa), a(last)
+
+
+def gpu_step(wl, bufs, dev, use_layer_api=True, workspaces=None, k_packed=True, rope=None,
+             stacked=None, anchor_lag=0, tables="padded"):
     """Run setup + every layer on the GPU; returns (outputs list, control dict).
-    rope: optional (cos, sin) float32 numpy [B, D/2] rotation of the step."""
+    rope: optional (cos, sin) float32 numpy [B, D/2] rotation of the step.
+    stacked: one uint8 tensor holding every buffer back to back (the stacked
+    KV form; `bufs` are then views into it and the step is given only the
+    stacked tensor).  anchor_lag: the setup's window anchor lag.  tables:
+    "padded" (2-D tables) or "csr" (compressed page lists; the setup writes
+    the padded full table the layers read)."""
     c = wl.cfg
     d = device_inputs(wl, dev)
     rc, rs = (None, None) if rope is None else (torch.from_numpy(rope[0]).to(dev),
                                                  torch.from_numpy(rope[1]).to(dev))
     win = c.window if "swa" in c.kinds else 0
-    ctl = P.pkv_setup_attn_control(d["seq_lens"], d["active"], d["bt_full"], d["bt_swa"],
-                                   c.block, win, positions=d["positions"])
+    if tables == "csr":
+        ip, fi, si, lp = (torch.from_numpy(x).to(dev) for x in csr_lists(wl))
+        ctl = P.pkv_setup_attn_control_csr(ip, fi, si, lp, d["active"], c.block, win,
+                                           wl.bt_full.shape[1], positions=d["positions"],
+                                           anchor_lag=anchor_lag)
+        d["bt_full"] = ctl["bt_full"]
+    else:
+        ctl = P.pkv_setup_attn_control(d["seq_lens"], d["active"], d["bt_full"], d["bt_swa"],
+                                       c.block, win, positions=d["positions"],
+                                       anchor_lag=anchor_lag)
     sm = 1.0 / np.sqrt(c.head_dim)
     tw = ctl["bt_swa_trim"].shape[1]
     ws_full = P.new_workspace(c.batch, c.hq, c.hkv, c.head_dim, c.block, wl.bt_full.shape[1], 0, dev)
     ws_swa = P.new_workspace(c.batch, c.hq, c.hkv, c.head_dim, c.block, tw, win, dev) if win else None
     outs = []
     if use_layer_api and alternating(c):
-        step = P.make_step(bufs, ctl, d["bt_full"], c.batch, c.hq, c.hkv, c.head_dim, c.block,
-                           c.window, wl.nb, k_packed=k_packed, rope_cos=rc, rope_sin=rs)
+        step = P.make_step(None if stacked is not None else bufs, ctl, d["bt_full"], c.batch,
+                           c.hq, c.hkv, c.head_dim, c.block, c.window, wl.nb, k_packed=k_packed,
+                           stacked=stacked, rope_cos=rc, rope_sin=rs)
         for i in range(c.layers):
             out = torch.empty_like(d["q"][i])
             ws = ws_swa if i % 2 == 0 else ws_full
@@ -119,7 +170,7 @@ def gpu_step(wl, bufs, dev, use_layer_api=True, workspaces=None, k_packed=True, 
     return outs, ctl
 
 
-def oracle_step(wl, snaps, layers=None, k_packed=True, rope=None):
+def oracle_step(wl, snaps, layers=None, k_packed=True, rope=None, anchor_lag=0):
     """snaps: list of host uint8 arrays (whole buffers, pre-step).  Updated in place."""
     c = wl.cfg
     half = wl.half_bytes
@@ -131,21 +182,45 @@ def oracle_step(wl, snaps, layers=None, k_packed=True, rope=None):
                           c.block, c.hkv, c.window, wl.k_scale, wl.v_scale,
                           1.0 / np.sqrt(c.head_dim), k_packed, layers=layers, kinds=list(c.kinds),
                           rope_cos=None if rope is None else rope[0],
-                          rope_sin=None if rope is None else rope[1])
+                          rope_sin=None if rope is None else rope[1], anchor_lag=anchor_lag)
 
 
-def assert_close(got_bf16, ref, what=""):
+def bf16_ulp(x):
+    """Spacing of bf16 numbers at |x| (8 significant bits; 2^-133 below the
+    normal range)."""
+    a = np.maximum(np.abs(np.asarray(x, dtype=np.float64)), 2.0 ** -126)
+    _, e = np.frexp(a)              # a = m * 2^e, m in [0.5, 1)
+    return np.ldexp(1.0, e - 8)
+
+
+def assert_close(got_bf16, ref, what="", ulp_guard=ULP_GUARD, l2_guard=L2_GUARD):
     g = got_bf16.float().cpu().numpy().astype(np.float64)
     assert g.shape == ref.shape, (g.shape, ref.shape)
-    bad = ~(np.abs(g - ref) <= ATOL + RTOL * np.abs(ref))
+    err = np.abs(g - ref)
+    bad = ~(err <= ATOL + RTOL * np.abs(ref))
     if bad.any():
         idx = np.argwhere(bad)[:5]
-        err = np.abs(g - ref)
         raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside tolerance; "
                              f"max abs err {err[np.isfinite(err)].max() if np.isfinite(err).any() else 'nan'}; "
                              f"first {idx.tolist()} got {[g[tuple(i)] for i in idx]} "
                              f"ref {[ref[tuple(i)] for i in idx]}")
-    return float(np.max(np.abs(g - ref))) if g.size else 0.0
+    if not g.size:
+        return 0.0
+    ulp = bf16_ulp(ref)
+    ulps = np.max(np.maximum(err - FLOOR_GUARD, 0.0) / ulp)
+    raw_ulps = np.max(err / ulp)
+    l2 = float(np.sqrt(np.sum(err ** 2) / max(np.sum(ref ** 2), 1e-300)))
+    STATS.append((what, float(err.max()), float(ulps), l2, float(raw_ulps)))
+    print(f"[close] {what}: max abs {err.max():.2e}, max ulps beyond floor {ulps:.2f}, "
+          f"max ulps {raw_ulps:.2f}, rel L2 {l2:.2e}", flush=True)
+    tight = err <= ulp_guard * ulp + FLOOR_GUARD if ulp_guard is not None else np.ones_like(err, bool)
+    if not tight.all():
+        i = tuple(np.argwhere(~tight)[0])
+        raise AssertionError(f"{what}: {int((~tight).sum())} of {tight.size} beyond "
+                             f"{ulp_guard} bf16 ulps + {FLOOR_GUARD:.1e}; first {list(i)} got {g[i]} "
+                             f"ref {ref[i]}")
+    assert l2 <= l2_guard, f"{what}: relative L2 error {l2:.3e} above {l2_guard:.1e}"
+    return float(err.max())
 
 
 def sampled_blocks(wl, rows):

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert P.pkv_abi_version() == P.ABI_VERSION == 2
+    assert P.pkv_abi_version() == P.ABI_VERSION == 3
 
 
 @pytest.mark.parametrize("nb,H,Bk,D", [(36175, 1, 128, 64), (20880, 8, 32, 64), (7, 3, 16, 64)])
@@ -42,6 +42,9 @@ def test_buffer_bytes_match_oracle(nb, H, Bk, D):
 @pytest.mark.parametrize("Bk", [16, 32, 64, 128])
 def test_trimmed_width_matches_oracle(Bk):
     assert P.pkv_trimmed_width(128, Bk) == C.trimmed_width(128, Bk)
+    for w in (1, 17, 100, 128, 129):
+        for lag in (0, 1):
+            assert P.pkv_trimmed_width(w, Bk, lag) == C.trimmed_width(w, Bk, lag), (w, lag)
 
 
 def _attn(**over):
@@ -91,8 +94,13 @@ def test_update_and_setup_argument_errors():
                                  None, None, 0.1, 0.1, None) == P.PKV_ERR_ARG
     assert L.pkv_kv_cache_update(0, 1, 64, 16, 4, None, None, None, 1, None, None,
                                  None, None, 0.1, 0.1, None) == P.PKV_OK
-    assert L.pkv_setup_attn_control(1, 16, 128, None, None, None, None, 4, None, 4, 4, None,
+    assert L.pkv_setup_attn_control(1, 16, 128, 0, None, None, None, None, 4, None, 4, 4, None,
                                     None, None, 9, None, None, None, None) == P.PKV_ERR_ARG
+    # anchor_lag other than 0 or 1 is refused before anything else
+    assert L.pkv_setup_attn_control(1, 16, 128, 2, 0x100, 0x100, None, 0x100, 4, 0x100, 4, 4,
+                                    0x100, 0x100, 0x100, 9, 0x100, 0x100, None,
+                                    None) == P.PKV_ERR_ARG
+    assert b"anchor_lag" in L.pkv_last_error()
 
 
 def test_workspace_sizing():

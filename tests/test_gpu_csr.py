@@ -6,7 +6,7 @@ import torch
 
 import paged_fp8_kv_amd as P
 import workloads as W
-from gpu_harness import device_inputs
+from gpu_harness import assert_close, device_inputs, gpu_step, oracle_step, poison_stale
 from oracle import control as OC
 
 pytestmark = pytest.mark.gpu
@@ -70,3 +70,45 @@ def test_csr_tables_drive_identical_attention(gpu):
         outs.append((full, swa))
     torch.cuda.synchronize()
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+@pytest.mark.parametrize("name", ["cfg2", "cfg4", "cfg5"])
+def test_csr_control_matches_oracle(name, gpu):
+    """The control built from page lists against the oracle's control of the
+    oracle's own conversion of the same lists (not against the padded HIP
+    setup)."""
+    cfg = W.CONFIGS[name]
+    wl = W.make_workload(cfg, hbm_bytes=torch.cuda.mem_get_info(gpu)[1])
+    win = cfg.window if "swa" in cfg.kinds else 0
+    ip, fi, si, lp = _csr(wl)
+    width = wl.bt_full.shape[1]
+    t = lambda x: torch.from_numpy(x).to(gpu)
+    got = P.pkv_setup_attn_control_csr(t(ip), t(fi), t(si), t(lp), t(wl.active), cfg.block, win,
+                                       width, positions=t(wl.positions.astype(np.int64)))
+    torch.cuda.synchronize()
+    sl, bf, bs = OC.csr_to_tables(ip, fi, si if win else None, lp, cfg.block, width)
+    ref = OC.attention_control(sl, wl.active, bf, bs, cfg.block, max(win, 1),
+                               positions=wl.positions)
+    keys = ["pos_full", "upd_full", "pos_abs"] + (["pos_swa", "upd_swa", "bt_swa_trim"] if win else [])
+    for k in keys:
+        assert np.array_equal(got[k].cpu().numpy(), ref[k]), k
+    assert np.array_equal(got["seq_lens"].cpu().numpy(), sl)
+    assert np.array_equal(got["bt_full"].cpu().numpy(), bf)
+
+
+@pytest.mark.parametrize("name", ["cfg2", "cfg5"])
+def test_csr_step_matches_oracle(name, gpu):
+    """A whole step driven by page lists, against the oracle."""
+    print(f"[csr step] {name}", flush=True)
+    wl = W.make_workload(W.CONFIGS[name])
+    host = W.make_buffers(wl, "cpu")
+    poison_stale(host, wl)
+    snaps = [h.numpy().copy() for h in host]
+    bufs = [h.to(gpu) for h in host]
+    outs, _ = gpu_step(wl, bufs, gpu, tables="csr")
+    ref, _ = oracle_step(wl, snaps)
+    for i in range(wl.cfg.layers):
+        assert_close(outs[i], ref[i], f"{name} csr layer {i}")
+    for j, b in enumerate(bufs):
+        got = b.cpu().numpy()
+        assert np.array_equal(got, snaps[j]), f"buffer {j}: {int((got != snaps[j]).sum())} bytes differ"

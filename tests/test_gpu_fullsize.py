@@ -1,7 +1,9 @@
 """Parity at the full workload sizes, in the configuration the benchmark times
 (the layer entry point with its default split and workspace): the whole step
-runs on the GPU; the oracle recomputes a sample of sequences from a copy of
-the blocks they reference, taken before the step."""
+runs on the GPU; the oracle recomputes every sequence from a copy of the
+blocks the step references, taken before the step.  Repeated steps must give
+the same outputs bit for bit (the split merges cut items across workgroups
+through the workspace; a race there would show as a difference)."""
 import numpy as np
 import pytest
 import torch
@@ -12,50 +14,115 @@ from gpu_harness import (assert_close, gather_blocks, gpu_step, mini_workload, o
 
 pytestmark = pytest.mark.gpu
 
+REPEATS = 20
 
-def _run(name, rows_fn, layers, gpu):
+
+class _Case:
+    pass
+
+
+def _setup(name, gpu):
     cfg = W.CONFIGS[name]
     hbm = torch.cuda.mem_get_info(gpu)[1]
     wl = W.make_workload(cfg, hbm_bytes=hbm)
-    rows = rows_fn(wl)
-    print(f"[fullsize] {name}: nb={wl.nb} rows={rows.tolist()} layers={layers}", flush=True)
+    rows = np.arange(cfg.batch)
+    print(f"[fullsize] {name}: nb={wl.nb}, all {rows.size} sequences, {cfg.layers} layers",
+          flush=True)
     bufs = []
     for j in range(cfg.n_buffers):
         t = torch.empty(2 * wl.half_bytes, dtype=torch.uint8, device=gpu)
         W.fill_buffer(t, wl, j)
         bufs.append(t)
-    blocks = sampled_blocks(wl, rows)
-    before = [gather_blocks(b, wl, blocks) for b in bufs]
-    outs, _ = gpu_step(wl, bufs, gpu)
-    after = [gather_blocks(b, wl, blocks) for b in bufs]
-    mini = mini_workload(wl, rows, blocks)
-    ref, _ = oracle_step(mini, before, layers=set(layers))   # updates `before` in place
-    worst = 0.0
-    for i in layers:
-        got = outs[i][torch.from_numpy(rows).to(gpu)]
-        worst = max(worst, assert_close(got, ref[i][rows], f"{name} layer {i} rows {rows.tolist()}"))
-    # every byte of the sampled blocks (the new tokens' slots included)
-    for j in range(cfg.n_buffers):
-        assert np.array_equal(after[j], before[j]), \
-            f"{name} buffer {j}: {int((after[j] != before[j]).sum())} bytes differ"
-    print(f"[fullsize] {name}: max abs err {worst:.2e}", flush=True)
+    c = _Case()
+    c.wl, c.bufs, c.rows = wl, bufs, rows
+    c.blocks = sampled_blocks(wl, rows)
+    c.first = None
+    return c
+
+
+def _teardown(c):
     # hand the pool back now: the driver's clean-up of tens of GB of freed
     # device memory slows later bandwidth-bound work for some seconds, so let
     # it overlap the rest of the session rather than what runs after it
-    del bufs, outs
+    c.bufs.clear()
+    c.first = None
     torch.cuda.empty_cache()
 
 
-def test_fullsize_36_layer_batch64(gpu):
-    """36 alternating layers, batch 64, 8192-token contexts: two sequences,
-    the first and the last pair of layers."""
-    _run("cfg3", lambda wl: np.array([5, 63]), [0, 1, 34, 35], gpu)
+@pytest.fixture(scope="module")
+def cfg3(gpu):
+    c = _setup("cfg3", gpu)
+    yield c
+    _teardown(c)
 
 
-def test_fullsize_ragged_batch128_large_pool(gpu):
-    """Batch 128, log-uniform 128..32768 contexts, pool at 30% of HBM: the
-    longest, the shortest and a middle sequence."""
-    def rows(wl):
-        o = np.argsort(wl.seq_lens, kind="stable")
-        return np.array(sorted({int(o[-1]), int(o[0]), int(o[len(o) // 2])}))
-    _run("cfg4", rows, [0], gpu)
+@pytest.fixture(scope="module")
+def cfg4(gpu):
+    c = _setup("cfg4", gpu)
+    yield c
+    _teardown(c)
+
+
+def _parity(c, gpu):
+    wl, cfg = c.wl, c.wl.cfg
+    before = [gather_blocks(b, wl, c.blocks) for b in c.bufs]
+    outs, _ = gpu_step(wl, c.bufs, gpu)
+    c.first = outs
+    after = [gather_blocks(b, wl, c.blocks) for b in c.bufs]
+    mini = mini_workload(wl, c.rows, c.blocks)
+    worst = 0.0
+    # one pair of layers (one shared buffer) at a time keeps host memory and
+    # progress output bounded; the schedule inside a pair is the oracle's own
+    for j in range(cfg.n_buffers):
+        lay = [i for i in (2 * j, 2 * j + 1) if i < cfg.layers]
+        sub = mini_workload_pair(mini, lay)
+        ref, _ = oracle_step(sub, [before[j]])        # updates before[j] in place
+        for k, i in enumerate(lay):
+            worst = max(worst, assert_close(outs[i], ref[k], f"{cfg.name} layer {i}, all rows"))
+        assert np.array_equal(after[j], before[j]), \
+            f"{cfg.name} buffer {j}: {int((after[j] != before[j]).sum())} bytes differ"
+        print(f"[fullsize] {cfg.name}: buffer {j} done (max abs err so far {worst:.2e})",
+              flush=True)
+
+
+def mini_workload_pair(wl, layers):
+    """The workload restricted to the given consecutive layers (one shared
+    buffer): their queries, new tokens, scales and kinds."""
+    import dataclasses
+    cfg = dataclasses.replace(wl.cfg, kinds=tuple(wl.cfg.kinds[i] for i in layers))
+    return dataclasses.replace(wl, cfg=cfg, q=wl.q[layers], k_new=wl.k_new[layers],
+                               v_new=wl.v_new[layers], k_scale=[wl.k_scale[i] for i in layers],
+                               v_scale=[wl.v_scale[i] for i in layers])
+
+
+def _repeats(c, gpu):
+    assert c.first is not None, "run after the parity test of the same workload"
+    for r in range(REPEATS):
+        outs, _ = gpu_step(c.wl, c.bufs, gpu)
+        for i, (a, b) in enumerate(zip(c.first, outs)):
+            if not torch.equal(a.view(torch.int16), b.view(torch.int16)):
+                diff = (a.view(torch.int16) != b.view(torch.int16)).nonzero()[:5].tolist()
+                raise AssertionError(f"{c.wl.cfg.name}: repeat {r} layer {i} differs at {diff}")
+    print(f"[fullsize] {c.wl.cfg.name}: {REPEATS} repeated steps bitwise identical", flush=True)
+
+
+@pytest.mark.timeout(900)
+def test_fullsize_36_layer_batch64_every_row_every_layer(cfg3, gpu):
+    """36 alternating layers, batch 64, 8192-token contexts: every sequence of
+    every layer against the oracle, every byte of every referenced block."""
+    _parity(cfg3, gpu)
+
+
+def test_fullsize_36_layer_batch64_repeats_bitwise(cfg3, gpu):
+    _repeats(cfg3, gpu)
+
+
+@pytest.mark.timeout(600)
+def test_fullsize_ragged_batch128_large_pool_every_row(cfg4, gpu):
+    """Batch 128, log-uniform 128..32768 contexts, pool at 30% of HBM: every
+    sequence against the oracle."""
+    _parity(cfg4, gpu)
+
+
+def test_fullsize_ragged_batch128_repeats_bitwise(cfg4, gpu):
+    _repeats(cfg4, gpu)

@@ -229,3 +229,21 @@ def test_packed_and_unpacked_k_agree_bitwise(name, gpu):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
     for x, y in zip(bufs, unp):
         assert torch.equal(packed_to_unpacked(x, wl), y)
+
+
+@pytest.mark.parametrize("name", ["cfg1", "cfg2", "cfg5"])
+def test_step_matches_oracle_at_non_power_of_two_scales(name, gpu):
+    """k_scale 0.0173 and v_scale 0.0411 (not powers of two, so the
+    quantising division rounds and the scales do not factor out exactly)."""
+    import dataclasses
+    print(f"[parity scales] {name}", flush=True)
+    wl, bufs, snaps = _small_case(name, gpu)
+    n = wl.cfg.layers
+    wl = dataclasses.replace(wl, k_scale=[0.0173] * n, v_scale=[0.0411] * n)
+    outs, _ = gpu_step(wl, bufs, gpu)
+    ref, _ = oracle_step(wl, snaps)
+    for i in range(n):
+        assert_close(outs[i], ref[i], f"{name} scales layer {i}")
+    for j, b in enumerate(bufs):
+        got = b.cpu().numpy()
+        assert np.array_equal(got, snaps[j]), f"{name} buffer {j}: {int((got != snaps[j]).sum())} bytes differ"

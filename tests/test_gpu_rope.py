@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import workloads as W
-from gpu_harness import assert_close, gpu_step, oracle_step, poison_stale
+from gpu_harness import ROPE_GUARDS, assert_close, gpu_step, oracle_step, poison_stale
 from oracle import control as OC
 from oracle import layout as OL
 from paged_build import rope_fma_trap
@@ -25,7 +25,7 @@ def _case(name, gpu):
 
 def _check(wl, outs, bufs, ref, snaps, what):
     for i in range(wl.cfg.layers):
-        assert_close(outs[i], ref[i], f"{what} layer {i}")
+        assert_close(outs[i], ref[i], f"{what} layer {i}", **ROPE_GUARDS)
     for j, b in enumerate(bufs):
         got = b.cpu().numpy()
         assert np.array_equal(got, snaps[j]), f"{what} buffer {j}: {int((got != snaps[j]).sum())} bytes differ"
