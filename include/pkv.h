@@ -268,6 +268,21 @@ int pkv_decode_layer(const pkv_step* step, int32_t layer, const uint16_t* q,
                      float v_scale, float sm_scale, uint16_t* out, void* workspace,
                      int64_t workspace_bytes, void* stream);
 
+/* pkv_decode_layer without a workspace argument, for callers that cannot
+ * allocate device memory (work under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results and bytes as
+ * pkv_decode_layer; the split-KV workspace is instead a 24 MiB array the
+ * library holds on each GPU it runs on, from its first use there until the
+ * process ends.  Shapes whose pkv_decode_workspace_bytes exceeds 24 MiB are
+ * refused with PKV_ERR_WORKSPACE before anything is enqueued.  Each call
+ * clears the part of the array that must start at zero (one small extra
+ * kernel on `stream`) and allocates nothing.  Every call on a GPU shares
+ * that GPU's array: calls that overlap on one GPU (other streams, other
+ * threads) race and must be serialised by the caller. */
+int pkv_decode_layer_noalloc(const pkv_step* step, int32_t layer, const uint16_t* q,
+                             const uint16_t* k_new, const uint16_t* v_new, float k_scale,
+                             float v_scale, float sm_scale, uint16_t* out, void* stream);
+
 /* Debug check of the control tables (synchronous: copies them to the host).
  * Checks every table entry a step would read: ids in [0, num_blocks) for the
  * keys of each active sequence in both tables, full and sliding-window ids

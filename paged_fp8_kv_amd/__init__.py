@@ -65,6 +65,8 @@ _SIGS = {
                                _vp], _i32),
     "pkv_decode_layer": ([ctypes.POINTER(PkvStep), _i32, _vp, _vp, _vp, _f32, _f32, _f32, _vp,
                           _vp, _i64, _vp], _i32),
+    "pkv_decode_layer_noalloc": ([ctypes.POINTER(PkvStep), _i32, _vp, _vp, _vp, _f32, _f32, _f32,
+                                  _vp, _vp], _i32),
     "pkv_validate_attn_control": ([_i32, _i32, _i32, _i64, _vp, _vp, _vp, _i32, _vp, _i32,
                                    _i32, _vp], _i32),
 }
@@ -330,6 +332,17 @@ def pkv_decode_layer(step, layer, q, k_new, v_new, k_scale, v_scale, sm_scale, o
         _dev_ptr(k_new, torch.bfloat16, "k_new"), _dev_ptr(v_new, torch.bfloat16, "v_new"),
         float(k_scale), float(v_scale), float(sm_scale), _dev_ptr(out, torch.bfloat16, "out"),
         _dev_ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
+    return out
+
+
+def pkv_decode_layer_noalloc(step, layer, q, k_new, v_new, k_scale, v_scale, sm_scale, out,
+                             stream=None):
+    """pkv_decode_layer with the library's own workspace (no allocation)."""
+    _check(lib().pkv_decode_layer_noalloc(
+        ctypes.byref(step), layer, _dev_ptr(q, torch.bfloat16, "q"),
+        _dev_ptr(k_new, torch.bfloat16, "k_new"), _dev_ptr(v_new, torch.bfloat16, "v_new"),
+        float(k_scale), float(v_scale), float(sm_scale), _dev_ptr(out, torch.bfloat16, "out"),
+        _stream(stream)))
     return out
 
 

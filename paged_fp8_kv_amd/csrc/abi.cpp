@@ -280,7 +280,8 @@ static int attn_impl(int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t h
                      const int32_t* frame_pos, float k_scale, float v_scale, float sm_scale,
                      uint16_t* out, void* workspace, int64_t workspace_bytes, void* stream,
                      const uint16_t* k_new, const uint16_t* v_new, uint8_t* k_w, uint8_t* v_w,
-                     const int64_t* upd, const float* rope_cos, const float* rope_sin) {
+                     const int64_t* upd, const float* rope_cos, const float* rope_sin,
+                     bool use_scratch = false) {
   if (batch < 0) return fail(PKV_ERR_ARG, "batch must be >= 0");
   if (batch == 0) return ok();
   if (batch > pkv::kMaxBatch)
@@ -321,10 +322,17 @@ static int attn_impl(int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t h
   const int ms = pkv::attn_max_subtiles(block, table_width, window);
   const int w = pkv::attn_workers(batch, kv_heads, ms);
   const int64_t need = pkv::attn_workspace_bytes(batch, kv_heads, w);
-  if (!workspace || workspace_bytes < need)
-    return fail(PKV_ERR_WORKSPACE, "workspace of %lld bytes needed (got %lld)", (long long)need,
-                (long long)workspace_bytes);
-  if (!aligned(workspace, 256)) return fail(PKV_ERR_ARG, "workspace must be 256-byte aligned");
+  if (use_scratch) {
+    if (need > pkv::kScratchBytes)
+      return fail(PKV_ERR_WORKSPACE,
+                  "these shapes need %lld bytes of workspace; the library's own holds %lld",
+                  (long long)need, (long long)pkv::kScratchBytes);
+  } else {
+    if (!workspace || workspace_bytes < need)
+      return fail(PKV_ERR_WORKSPACE, "workspace of %lld bytes needed (got %lld)", (long long)need,
+                  (long long)workspace_bytes);
+    if (!aligned(workspace, 256)) return fail(PKV_ERR_ARG, "workspace must be 256-byte aligned");
+  }
   pkv::AttnLaunch L{};
   L.q = q;
   L.k = k_half;
@@ -353,6 +361,9 @@ static int attn_impl(int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t h
   L.upd = upd;
   L.rope_cos = rope_cos;
   L.rope_sin = rope_sin;
+  if (use_scratch)
+    return hip_status(pkv::launch_decode_attn_scratch(L, static_cast<hipStream_t>(stream)),
+                      "attention launch");
   return hip_status(pkv::launch_decode_attn(L, static_cast<hipStream_t>(stream)), "attention launch");
 }
 
@@ -369,9 +380,10 @@ int pkv_paged_decode_attn(int32_t batch, int32_t q_heads, int32_t kv_heads, int3
                    nullptr, nullptr, nullptr, rope_cos, rope_sin);
 }
 
-int pkv_decode_layer(const pkv_step* s, int32_t layer, const uint16_t* q, const uint16_t* k_new,
-                     const uint16_t* v_new, float k_scale, float v_scale, float sm_scale,
-                     uint16_t* out, void* workspace, int64_t workspace_bytes, void* stream) {
+static int decode_layer_impl(const pkv_step* s, int32_t layer, const uint16_t* q,
+                             const uint16_t* k_new, const uint16_t* v_new, float k_scale,
+                             float v_scale, float sm_scale, uint16_t* out, void* workspace,
+                             int64_t workspace_bytes, void* stream, bool use_scratch) {
   if (!s) return fail(PKV_ERR_ARG, "null step");
   if (layer < 0 || layer / 2 >= s->n_buffers)
     return fail(PKV_ERR_ARG, "layer %d has no buffer (n_buffers %d)", layer, s->n_buffers);
@@ -407,11 +419,26 @@ int pkv_decode_layer(const pkv_step* s, int32_t layer, const uint16_t* q, const 
     return attn_impl(s->batch, s->q_heads, s->kv_heads, s->head_dim, s->block, s->num_blocks,
                      s->window, q, kh, s->k_packed, vh, s->bt_swa_trim, s->trim_width,
                      s->trim_width, s->pos_swa, k_scale, v_scale, sm_scale, out, workspace,
-                     workspace_bytes, stream, k_new, v_new, kh, vh, upd, s->rope_cos, s->rope_sin);
+                     workspace_bytes, stream, k_new, v_new, kh, vh, upd, s->rope_cos, s->rope_sin,
+                     use_scratch);
   return attn_impl(s->batch, s->q_heads, s->kv_heads, s->head_dim, s->block, s->num_blocks, 0, q,
                    kh, s->k_packed, vh, s->bt_full, s->bt_full_stride, s->bt_full_width,
                    s->pos_full, k_scale, v_scale, sm_scale, out, workspace, workspace_bytes, stream,
-                   k_new, v_new, kh, vh, upd, s->rope_cos, s->rope_sin);
+                   k_new, v_new, kh, vh, upd, s->rope_cos, s->rope_sin, use_scratch);
+}
+
+int pkv_decode_layer(const pkv_step* s, int32_t layer, const uint16_t* q, const uint16_t* k_new,
+                     const uint16_t* v_new, float k_scale, float v_scale, float sm_scale,
+                     uint16_t* out, void* workspace, int64_t workspace_bytes, void* stream) {
+  return decode_layer_impl(s, layer, q, k_new, v_new, k_scale, v_scale, sm_scale, out, workspace,
+                           workspace_bytes, stream, false);
+}
+
+int pkv_decode_layer_noalloc(const pkv_step* s, int32_t layer, const uint16_t* q,
+                             const uint16_t* k_new, const uint16_t* v_new, float k_scale,
+                             float v_scale, float sm_scale, uint16_t* out, void* stream) {
+  return decode_layer_impl(s, layer, q, k_new, v_new, k_scale, v_scale, sm_scale, out, nullptr, 0,
+                           stream, true);
 }
 
 int pkv_validate_attn_control(int32_t batch, int32_t block, int32_t window, int64_t num_blocks,

@@ -1350,4 +1350,56 @@ hipError_t launch_decode_attn(const AttnLaunch& L, hipStream_t stream) {
   }
 }
 
+// ---- the library's own workspace, for pkv_decode_layer_noalloc -------------
+// Callers that cannot allocate device memory (work under HIP graph capture,
+// tight serving loops) get the split-KV workspace from this array instead of
+// an argument.  Each GPU the library runs on holds its own copy until the
+// process ends; every call on a GPU shares it, so calls that overlap on one
+// GPU race.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+__global__ void __launch_bounds__(256) zero_words_kernel(uint32_t* p, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+}  // namespace
+
+hipError_t attn_scratch(void** ptr) {
+  // The array's name is a host-side stand-in: its device address is looked
+  // up once per device, with that device current, and kept.
+  static std::atomic<void*> addr[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  void* p = (dev >= 0 && dev < 64) ? addr[dev].load(std::memory_order_acquire) : nullptr;
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    if (dev >= 0 && dev < 64) addr[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
+}
+
+hipError_t launch_decode_attn_scratch(const AttnLaunch& L0, hipStream_t stream) {
+  if (attn_workspace_bytes(L0.B, L0.Hkv, L0.n_workers) > kScratchBytes) return hipErrorInvalidValue;
+  void* p = nullptr;
+  hipError_t e = attn_scratch(&p);
+  if (e != hipSuccess) return e;
+  AttnLaunch L = L0;
+  L.workspace = p;
+  // the arrival counters must start at zero: clear them on every call (a
+  // fill kernel rather than a memset node, so the call can be captured)
+  const int64_t words = counters_bytes(L.B, L.Hkv) / 4;
+  hipLaunchKernelGGL(zero_words_kernel, dim3(static_cast<unsigned>((words + 255) / 256)), dim3(256),
+                     0, stream, static_cast<uint32_t*>(p), words);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_decode_attn(L, stream);
+}
+
 }  // namespace pkv

@@ -48,6 +48,13 @@ int attn_workers(int64_t batch, int kv_heads, int max_subtiles);
 int64_t attn_workspace_bytes(int64_t batch, int kv_heads, int n_workers);
 hipError_t launch_decode_attn(const AttnLaunch& L, hipStream_t stream);
 
+// Bytes of the library's own device workspace (one per GPU), used by
+// launch_decode_attn_scratch in place of L.workspace: launches needing more
+// are refused.  attn_scratch gives the current device's copy.
+constexpr int64_t kScratchBytes = int64_t{24} << 20;
+hipError_t attn_scratch(void** ptr);
+hipError_t launch_decode_attn_scratch(const AttnLaunch& L, hipStream_t stream);
+
 struct SetupLaunch {
   int32_t B, block, window;
   int32_t anchor_lag;  // 0, or 1: the window frame is anchored at p - 1

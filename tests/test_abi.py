@@ -124,3 +124,24 @@ def test_decode_layer_rejects_both_or_neither_kv_form():
     st = P.lib().pkv_decode_layer(ctypes.byref(s), 0, None, None, None, 0.1, 0.1, 0.1, None,
                                   None, 0, None)
     assert st == P.PKV_ERR_ARG and b"exactly one" in P.lib().pkv_last_error()
+
+
+def test_noalloc_refuses_shapes_beyond_its_workspace():
+    """The no-allocation layer call holds a 24 MiB workspace per GPU: shapes
+    needing more are refused on the host, before anything is enqueued."""
+    L = P.lib()
+    s = P.PkvStep()
+    s.batch, s.q_heads, s.kv_heads, s.head_dim, s.block = 8192, 256, 256, 64, 32
+    s.window, s.num_blocks, s.n_buffers, s.k_packed = 128, 4, 1, 1
+    ka = (ctypes.c_void_p * 1)(0x10000)
+    va = (ctypes.c_void_p * 1)(0x20000)
+    s.k_bufs = ctypes.cast(ka, ctypes.POINTER(ctypes.c_void_p))
+    s.v_bufs = ctypes.cast(va, ctypes.POINTER(ctypes.c_void_p))
+    s.bt_full = s.bt_swa_trim = s.pos_full = s.pos_swa = s.upd_full = s.upd_swa = 0x1000
+    s.bt_full_stride = s.bt_full_width = 256
+    s.trim_width = 5
+    need = P.pkv_decode_workspace_bytes(8192, 256, 256, 64, 32, 256, 0)
+    assert need > 24 << 20
+    st = L.pkv_decode_layer_noalloc(ctypes.byref(s), 1, 0x1000, 0x1000, 0x1000, 0.125, 0.0625,
+                                    0.125, 0x1000, None)
+    assert st == P.PKV_ERR_WORKSPACE and b"library's own" in L.pkv_last_error()
