@@ -17,8 +17,11 @@ of the read probes of libpkv_probe on a 4 GiB buffer: one stream, and whole
 tiles of the kernel's tile size (block x head_dim bytes) in a scrambled order,
 over a few launch sizes with plain and non-temporal loads.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config cfgN]
     python bench.py --calibrate-copy      # plain device copy, for counter scaling
+
+The all-core CPU baseline starts worker processes; under a profiler that
+preloads a GPU library into child processes, pass --no-cpu-baseline.
 """
 import argparse
 import hashlib
@@ -110,41 +113,116 @@ def hbm_ceiling(dev, tile_bytes, reps=10, nbytes=1 << 32):
             "best_launch": {k: {"grid": v[1], "nontemporal": bool(v[2])} for k, v in best.items()}}
 
 
-def cpu_baseline(wl, bufs_dev, seconds):
+def _oracle_rows(task):
+    """Worker of the all-core CPU baseline: the oracle's paged attention for
+    one sequence of one full-attention layer, reading the layer's referenced
+    blocks from a memory-mapped file.  Returns the KV bytes attended."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention as OA
+    path, half, q, table, pos, block, hkv, ks, vs, sm, nbytes = task
+    buf = np.memmap(path, dtype=np.uint8, mode="r")
+    with threadpool_limits(1):
+        OA.paged_decode_attention(q, buf[:half], buf[half:], table, pos, 0, block, hkv, ks, vs,
+                                  sm, True)
+    return nbytes
+
+
+def _host_blocks(buf, wl):
+    """Host copy of the blocks the full table references (both halves, in
+    the order of their ids) and the full table relabelled onto them."""
+    import torch
+    c = wl.cfg
+    ids = np.unique(wl.bt_full[wl.bt_full >= 0]).astype(np.int64)
+    per = c.hkv * c.block * c.head_dim
+    sel = buf.view(2, wl.nb, per).index_select(1, torch.from_numpy(ids).to(buf.device))
+    remap = np.full(wl.nb, -1, np.int64)
+    remap[ids] = np.arange(ids.size)
+    table = np.where(wl.bt_full >= 0, remap[np.maximum(wl.bt_full, 0)], -1).astype(np.int32)
+    return sel.cpu().numpy().reshape(-1), ids.size * per, table
+
+
+def cpu_baseline(wl, bufs_dev, seconds, workers):
     """Time the oracle's paged attention over the full-attention layers of the
-    step, sequence by sequence and layer after layer, until `seconds` of work
-    (single thread); reports KV bytes attended per second."""
+    step (float64 numpy, never tuned for speed), reported as KV GB/s attended.
+
+    One core: sequence after sequence, layer after layer, for `seconds`.
+    All cores: a pool of `workers` processes (spawned, CPU only) over the
+    (layer, sequence) pairs of the first full layers of the step, each
+    worker with one BLAS thread and the layers' referenced blocks
+    memory-mapped from files; the sample is sized to about `seconds` of
+    one-core work per worker.  Both run before any GPU timing."""
+    import multiprocessing as mp
+    import tempfile
+
     from threadpoolctl import threadpool_limits
 
     from oracle import attention as OA
     c = wl.cfg
     full_layers = [i for i, k in enumerate(c.kinds) if k == "full"]
     pos = (wl.seq_lens - 1).astype(np.int64)
-    half = wl.half_bytes
+    sm = 1.0 / np.sqrt(c.head_dim)
+    active = [b for b in range(c.batch) if wl.active[b]]
+    kv = lambda b: int(wl.seq_lens[b]) * c.hkv * 2 * c.head_dim
+    # ---- one core
     done_bytes, rows, layers, dt = 0, 0, 0, 0.0
     with threadpool_limits(1):
         for layer in full_layers:
-            host = bufs_dev[layer // 2].cpu().numpy()
-            kh, vh = host[:half], host[half:]
+            host, half, table = _host_blocks(bufs_dev[layer // 2], wl)
             q = wl.q[layer].float().numpy().astype(np.float64)
             layers += 1
             t0 = time.perf_counter()
-            for b in range(c.batch):
-                OA.paged_decode_attention(q, kh, vh, wl.bt_full, pos, 0, c.block, c.hkv,
-                                          wl.k_scale[layer], wl.v_scale[layer],
-                                          1.0 / np.sqrt(c.head_dim), True, rows=[b])
-                done_bytes += int(wl.seq_lens[b]) * c.hkv * 2 * c.head_dim
+            for b in active:
+                OA.paged_decode_attention(q, host[:half], host[half:], table, pos, 0, c.block,
+                                          c.hkv, wl.k_scale[layer], wl.v_scale[layer], sm, True,
+                                          rows=[b])
+                done_bytes += kv(b)
                 rows += 1
                 if dt + time.perf_counter() - t0 >= seconds:
                     break
             dt += time.perf_counter() - t0
-            del host, kh, vh
+            del host
             if dt >= seconds:
                 break
-    return {"value": round(done_bytes / dt / 1e9, 6), "unit": "GB/s", "cores": 1,
+    one = {"value": round(done_bytes / dt / 1e9, 6), "unit": "GB/s", "cores": 1,
+           "sample": f"{rows} sequence-layers over {layers} full-attention layers "
+                     f"({done_bytes / 1e6:.1f} MB of KV) in {dt:.1f} s"}
+    # ---- all cores: enough (layer, sequence) pairs for ~`seconds` per worker
+    target = done_bytes / dt * seconds * workers
+    tasks, staged, total = [], [], 0
+    tmpdir = tempfile.mkdtemp(prefix="pkv_cpu_")
+    try:
+        for layer in full_layers:
+            if total >= target:
+                break
+            host, half, table = _host_blocks(bufs_dev[layer // 2], wl)
+            path = os.path.join(tmpdir, f"layer{layer}.bin")
+            host.tofile(path)
+            staged.append(path)
+            del host
+            q = wl.q[layer].float().numpy().astype(np.float64)
+            for b in active:
+                tasks.append((path, half, q[b:b + 1], table[b:b + 1], pos[b:b + 1], c.block,
+                              c.hkv, wl.k_scale[layer], wl.v_scale[layer], sm, kv(b)))
+                total += kv(b)
+                if total >= target:
+                    break
+        with mp.get_context("spawn").Pool(workers) as pool:
+            pool.map(_oracle_rows, tasks[:workers], chunksize=1)   # start the workers
+            t0 = time.perf_counter()
+            got = sum(pool.map(_oracle_rows, tasks, chunksize=1))
+            wall = time.perf_counter() - t0
+    finally:
+        for pth in staged:
+            os.remove(pth)
+        os.rmdir(tmpdir)
+    return {"value": round(got / wall / 1e9, 6), "unit": "GB/s", "cores": workers,
             "kind": "oracle",
-            "sample": f"{rows} sequence-layers over {layers} full-attention layers "
-                      f"({done_bytes / 1e6:.1f} MB of KV) in {dt:.1f} s, numpy float64, 1 thread"}
+            "sample": f"{len(tasks)} sequence-layers over {len(staged)} full-attention layers "
+                      f"({got / 1e6:.1f} MB of KV) in {wall:.1f} s on {workers} worker processes "
+                      f"(numpy float64, 1 BLAS thread each; the host reports {os.cpu_count()} "
+                      f"CPUs)",
+            "one_core": one}
 
 
 def identity_tables(wl):
@@ -175,7 +253,11 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="cfg3")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
+                    help="seconds of oracle work per core (one-core run, and per worker)")
+    ap.add_argument("--cpu-workers", type=int, default=0,
+                    help="worker processes of the all-core oracle timing (default: the CPUs "
+                         "this process may use, at most 16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true",
@@ -308,7 +390,8 @@ def main():
     # was measured to slow this step by ~4% for about 20 s).
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, bufs, args.cpu_seconds)
+        workers = args.cpu_workers or min(16, len(os.sched_getaffinity(0)))
+        cpu = cpu_baseline(wl, bufs, args.cpu_seconds, workers)
 
     # eager warm-up; after the first step the cache holds this step's tokens,
     # so every later step recomputes identical outputs
@@ -424,7 +507,7 @@ def main():
         "data": "synthetic (seeded N(0,1) activations, FP8 history, random block tables)",
         "config": {"workload": cfg.name, "layers": cfg.layers, "batch": cfg.batch,
                    "q_heads": cfg.hq, "kv_heads": cfg.hkv, "head_dim": cfg.head_dim,
-                   "block": cfg.block, "context": "8192" if cfg.ctx[0] == "fixed" else str(cfg.ctx),
+                   "block": cfg.block, "context": str(cfg.ctx[1]) if cfg.ctx[0] == "fixed" else str(cfg.ctx),
                    "window": cfg.window, "num_blocks": wl.nb, "k_layout": args.k_layout, "tables": args.tables,
                    "rope": args.rope, "control": args.control, "graph": use_graph},
         "tokens_per_s": round(cfg.batch / (ms * 1e-3), 1),

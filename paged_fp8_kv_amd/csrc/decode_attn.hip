@@ -32,6 +32,7 @@
 //    beats it by more than 2^8, so rescaling is rare and the PV weights stay
 //    below 256 (exact bookkeeping: numerator and denominator share the
 //    reference maximum).
+#include <algorithm>
 #include <atomic>
 
 #include "pkv_device.hpp"
@@ -266,11 +267,13 @@ __device__ __forceinline__ void wait_vmcnt_slots(int n) {
   }
 }
 
-template <int BK, bool WINDOWED, bool KP>
+template <int BK, bool WINDOWED, bool KP, int NREG = kWinRegs>
 struct Item {
   // non-temporal K/V loads for full attention (measured: faster there, and
   // no gain for the short window reads)
   static constexpr bool kStreamNT = !WINDOWED;
+  static constexpr int kEntries = 64 * NREG;  // table entries held in registers
+  static constexpr int kBK = BK;
   const uint8_t* kbase;
   const uint8_t* vbase;
   uint8_t* kw;          // writable halves, for the fused new-token write
@@ -281,7 +284,7 @@ struct Item {
   int hkv, h;
   int clo, chi;         // first / last logical block holding keys
   int tab_base;         // logical block held by lane 0 of tab[0]
-  int tab[kWinRegs];    // table entries for logical blocks tab_base + 64 r + lane
+  int tab[NREG];        // table entries for logical blocks tab_base + 64 r + lane
   bool bad;
 
   __device__ Item(const AttnArgs& a, int b, int h_)
@@ -293,7 +296,7 @@ struct Item {
     trow = a.table + static_cast<int64_t>(b) * a.bt_stride;
     tab_base = -1000000;
 #pragma unroll
-    for (int r = 0; r < kWinRegs; ++r) tab[r] = 0;
+    for (int r = 0; r < NREG; ++r) tab[r] = 0;
   }
 
   // Keys lo .. hi: logical blocks lo/BK .. hi/BK.
@@ -302,14 +305,14 @@ struct Item {
     chi = hi / BK;
   }
 
-  // Load the table entries of logical blocks c0 .. c0+kWinEntries-1 (entries
+  // Load the table entries of logical blocks c0 .. c0+kEntries-1 (entries
   // past the row's width read as 0; only blocks clo .. chi are ever used).
   // Done between pipelined runs only, so no table load is ever pending while
   // K/V loads are in flight.
   __device__ __forceinline__ void load_window(int c0) {
     tab_base = c0;
 #pragma unroll
-    for (int r = 0; r < kWinRegs; ++r) {
+    for (int r = 0; r < NREG; ++r) {
       const int cc = c0 + 64 * r + lane_id();
       tab[r] = (cc < width) ? trow[cc] : 0;
     }
@@ -322,7 +325,7 @@ struct Item {
     const int sel = i >> 6;
     int blk = __builtin_amdgcn_readlane(tab[0], i & 63);
 #pragma unroll
-    for (int r = 1; r < kWinRegs; ++r) {
+    for (int r = 1; r < NREG; ++r) {
       const int br = __builtin_amdgcn_readlane(tab[r], i & 63);
       blk = (sel == r) ? br : blk;
     }
@@ -529,9 +532,9 @@ __device__ __forceinline__ void store_bf16x16(uint16_t* dst, const float* v) {
 // sub-tile and store the codes there; when it is -1, write nothing and read
 // the cache as it is (as the separate update would); any other value, or a
 // table id outside the pool, flags the item bad (NaN row) and writes nothing.
-template <int BK, bool WINDOWED, bool KP>
-__device__ __forceinline__ void write_new_token(Item<BK, WINDOWED, KP>& it, uint8_t* ring, int slot,
-                                                int hi, int64_t upd, uint32_t kcode,
+template <int BK, bool WINDOWED, bool KP, int NREG>
+__device__ __forceinline__ void write_new_token(Item<BK, WINDOWED, KP, NREG>& it, uint8_t* ring,
+                                                int slot, int hi, int64_t upd, uint32_t kcode,
                                                 uint32_t vcode) {
   if (upd < 0) return;
   const bool was_bad = it.bad;
@@ -768,6 +771,140 @@ __device__ __forceinline__ void rotate_queries(u32x4_t& q0, u32x4_t& q1, const f
   q1 = u32x4_t{r[4], r[5], r[6], r[7]};
 }
 
+// Expanded queries for the score MFMA: qx[i][k] holds q[g][16q + 4i + k]
+// (lane: g = m & 7, q = lane >> 4) in the 16-bit half of parity e = m >> 3,
+// zeros in the other half.
+__device__ __forceinline__ void expand_queries(const u32x4_t& q0, const u32x4_t& q1, int e,
+                                               uint32_t (&qx)[4][4]) {
+  const uint32_t qw[8] = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int d = 4 * i + k;  // dim 16q + d
+      const uint32_t bits = (qw[d >> 1] >> (16 * (d & 1))) & 0xffffu;
+      qx[i][k] = bits << (16 * e);
+    }
+}
+
+// FP8 codes of the new token's K and V at dimension `lane` (K turned first
+// when rotary cos/sin are given: the partner dimension lives in lane ^ 32,
+// so every lane of the wave must be here).
+template <bool ROPE>
+__device__ __forceinline__ void new_token_codes(const AttnArgs& a, uint16_t kn_bits,
+                                                uint16_t vn_bits, float kn_c, float kn_s,
+                                                uint32_t& kcode, uint32_t& vcode) {
+  const int lane = lane_id();
+  float kf = bf16_bits_to_f32(kn_bits);
+  if (ROPE)
+    kf = rope_turn(kf, bf16_bits_to_f32(static_cast<uint16_t>(__shfl_xor(static_cast<int>(kn_bits), 32))),
+                   kn_c, kn_s, lane >= kHeadDim / 2);
+  kcode = f32_to_e4m3_rne_sat(__fdiv_rn(kf, a.k_scale));
+  vcode = f32_to_e4m3_rne_sat(__fdiv_rn(bf16_bits_to_f32(vn_bits), a.v_scale));
+}
+
+__device__ __forceinline__ void reset_state(State& s) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) s.acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  s.m = -INFINITY;
+  s.l = 0.f;
+}
+
+// Two-stage software pipeline over the sub-tiles t0 .. tlast of one piece,
+// run per window of the item's table entries held in registers.  Ring of
+// kDepth slots: sub-tile k lives in slot (k - tw) % kDepth.  While sub-tile k
+// is computed from registers, sub-tile k+1 is read from its slot into the
+// other register stage and up to kDepth-1 later sub-tiles are in flight; slot
+// k is refilled once k has been consumed.  start_run() issues a run's first
+// loads; stream() consumes every sub-tile, starting further runs as needed.
+static_assert(kDepth % 2 == 0, "register stages alternate with the slot index");
+template <class It>
+struct Segment {
+  It& it;
+  uint8_t* ring;
+  int tw, twl, tlast, span;
+
+  __device__ __forceinline__ Segment(It& it_, uint8_t* ring_, int t0, int tlast_, int span0)
+      : it(it_), ring(ring_), tw(t0), twl(t0), tlast(tlast_), span(span0) {}
+
+  __device__ __forceinline__ void start_run() {
+    const int cw0 = it.clampc((tw * kSub) / It::kBK);
+    if (cw0 < it.tab_base || cw0 >= it.tab_base + It::kEntries) it.load_window(cw0);
+    const int cend = min(it.tab_base + It::kEntries, cw0 + span);  // first column past the run
+    twl = max(tw, min(tlast, (cend * It::kBK) / kSub - 1));
+    span = It::kEntries;
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d)
+      if (tw + d <= twl) it.issue(ring, d, tw + d);
+  }
+
+  // The first run must have been started.  t_new: the sub-tile holding the
+  // new token (its codes patched into the slot before it is read), or -1.
+  template <bool KP>
+  __device__ __forceinline__ void stream(float score_scale, int lo, int hi, int t_new,
+                                         int64_t upd, uint32_t kcode, uint32_t vcode,
+                                         const uint32_t (&qx)[4][4], State& s) {
+    for (bool first = true; tw <= tlast; first = false) {
+      if (!first) start_run();
+      Stage st[2];
+      wait_vmcnt_slots(min(twl - tw, kDepth - 1));
+      if (tw == t_new) write_new_token(it, ring, 0, hi, upd, kcode, vcode);
+      read_slot<KP>(ring, 0, st[0]);
+      for (int i = tw; i <= twl; i += kDepth) {
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) {
+          const int t32 = i + d;
+          if (t32 > twl) break;
+          // sub-tile t32+1 is complete once at most the sub-tiles issued after
+          // it (t32+2 .. min(twl, t32+kDepth-1)) are outstanding
+          if (t32 < twl) {
+            wait_vmcnt_slots(min(twl - t32 - 1, kDepth - 2));
+            if (t32 + 1 == t_new)
+              write_new_token(it, ring, (d + 1) % kDepth, hi, upd, kcode, vcode);
+            read_slot<KP>(ring, (d + 1) % kDepth, st[(d + 1) & 1]);
+          }
+          if (t32 * kSub >= lo && t32 * kSub + kSub - 1 <= hi)
+            compute_subtile<false>(st[d & 1], t32, lo, hi, score_scale, qx, s);
+          else
+            compute_subtile<true>(st[d & 1], t32, lo, hi, score_scale, qx, s);
+          if (t32 + kDepth <= twl) it.issue(ring, d, t32 + kDepth);
+        }
+      }
+      tw = twl + 1;
+    }
+    s.bad = it.bad;
+  }
+};
+
+// Reduce a piece's state across the parity halves of the wave: o[4r + tau] =
+// dim 16q + 4r + tau of query g (valid in the lanes with e == 0), the
+// denominator and whether a bad table entry was met.
+__device__ __forceinline__ void finish_piece(State& s, float (&o)[16], float& lsum, bool& bad) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s.acc[t][r] += __shfl_xor(s.acc[t][r], 8, 64);
+  lsum = wave_sum_same_g(s.l);
+  bad = __any(s.bad);
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) o[4 * r + t] = s.acc[t][r];
+}
+
+// Normalise and store a whole item's output rows (lanes with e == 0, g < G).
+__device__ __forceinline__ void store_whole(const AttnArgs& a, int b, int h, float (&o)[16],
+                                            float lsum, bool bad) {
+  const int lane = lane_id();
+  const int m = lane & 15, q = lane >> 4, e = m >> 3, g = m & 7;
+  if (e == 0 && g < a.G) {
+    const float f = bad ? NAN : a.v_scale / lsum;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[i] *= f;
+    store_bf16x16(a.out + (static_cast<int64_t>(b) * a.Hq + h * a.G + g) * kHeadDim + 16 * q, o);
+  }
+}
+
 // Workgroup LDS for partials of items cut once inside the workgroup: two
 // piece slots per wave (head piece, tail piece) and one arrival counter per
 // chunk of the workgroup.
@@ -875,46 +1012,19 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const Pre& s_pr
 
     const int t0 = lo / kSub + jr;
     const int tlast = t0 + segr - 1;
-    // Two-stage software pipeline over the segment's sub-tiles, run per
-    // window of kWinEntries table entries.
     // The first run of a segment is shortened by a per-wave amount so that the
     // waves of a workgroup reach their run boundaries (where the ring drains
     // and refills) at different times and cover each other's bubbles.
-    int span = __builtin_amdgcn_readfirstlane(kWinEntries - 16 * ((threadIdx.x >> 6) & 3));
-    int tw = t0, twl = t0;
-    // Ring of kDepth slots: sub-tile k lives in slot (k - tw) % kDepth.  While
-    // sub-tile k is computed from registers, sub-tile k+1 is read from its
-    // slot into the other register stage and up to kDepth-1 later sub-tiles
-    // are in flight; slot k is refilled once k has been consumed.
-    static_assert(kDepth % 2 == 0, "register stages alternate with the slot index");
-    auto start_run = [&]() {
-      const int cw0 = it.clampc((tw * kSub) / BK);
-      if (cw0 < it.tab_base || cw0 >= it.tab_base + kWinEntries) it.load_window(cw0);
-      const int cend = min(it.tab_base + kWinEntries, cw0 + span);  // first column past the run
-      twl = max(tw, min(tlast, (cend * BK) / kSub - 1));
-      span = kWinEntries;
-#pragma unroll
-      for (int d = 0; d < kDepth; ++d)
-        if (tw + d <= twl) it.issue(ring, d, tw + d);
-    };
+    Segment<Item<BK, WINDOWED, KP>> seg_run(
+        it, ring, t0, tlast,
+        __builtin_amdgcn_readfirstlane(kWinEntries - 16 * ((threadIdx.x >> 6) & 3)));
     // the first run's K/V loads go out before anything waits for the queries
     // or the new token's rows, so those loads overlap the ring fill
-    start_run();
+    seg_run.start_run();
 
     if (rope) rotate_queries(q0, q1, rc, rs, q >= 2);
-    // expanded queries: qx[i][k] holds q[g][16q + 4i + k] in the half of parity e
     uint32_t qx[4][4];
-    {
-      const uint32_t qw[8] = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int d = 4 * i + k;  // dim 16q + d
-          const uint32_t bits = (qw[d >> 1] >> (16 * (d & 1))) & 0xffffu;
-          qx[i][k] = bits << (16 * e);
-        }
-    }
+    expand_queries(q0, q1, e, qx);
 
     // The new token (frame position hi) is in sub-tile t_new; with a fused
     // write, the segment holding it quantises the token's K/V (lane j: dim j),
@@ -923,72 +1033,20 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const Pre& s_pr
     const int t_new = (a.k_new != nullptr && hi / kSub >= lo / kSub + jr &&
                        hi / kSub < lo / kSub + jr + segr) ? hi / kSub : -1;
     uint32_t kcode = 0, vcode = 0;
-    if (t_new >= 0) {
-      float kf = bf16_bits_to_f32(kn_bits);
-      if (rope)  // partner dimension lane ^ 32 (t_new is uniform: every lane is here)
-        kf = rope_turn(kf, bf16_bits_to_f32(static_cast<uint16_t>(__shfl_xor(static_cast<int>(kn_bits), 32))),
-                       kn_c, kn_s, lane >= kHeadDim / 2);
-      kcode = f32_to_e4m3_rne_sat(__fdiv_rn(kf, a.k_scale));
-      vcode = f32_to_e4m3_rne_sat(__fdiv_rn(bf16_bits_to_f32(vn_bits), a.v_scale));
-    }
+    if (t_new >= 0) new_token_codes<ROPE>(a, kn_bits, vn_bits, kn_c, kn_s, kcode, vcode);
     State s;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) s.acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    s.m = -INFINITY;
-    s.l = 0.f;
-
-    for (bool first = true; tw <= tlast; first = false) {
-      if (!first) start_run();
-      Stage st[2];
-      wait_vmcnt_slots(min(twl - tw, kDepth - 1));
-      if (tw == t_new) write_new_token(it, ring, 0, hi, upd_b, kcode, vcode);
-      read_slot<KP>(ring, 0, st[0]);
-      for (int i = tw; i <= twl; i += kDepth) {
-#pragma unroll
-        for (int d = 0; d < kDepth; ++d) {
-          const int t32 = i + d;
-          if (t32 > twl) break;
-          // sub-tile t32+1 is complete once at most the sub-tiles issued after
-          // it (t32+2 .. min(twl, t32+kDepth-1)) are outstanding
-          if (t32 < twl) {
-            wait_vmcnt_slots(min(twl - t32 - 1, kDepth - 2));
-            if (t32 + 1 == t_new)
-              write_new_token(it, ring, (d + 1) % kDepth, hi, upd_b, kcode, vcode);
-            read_slot<KP>(ring, (d + 1) % kDepth, st[(d + 1) & 1]);
-          }
-          if (t32 * kSub >= lo && t32 * kSub + kSub - 1 <= hi)
-            compute_subtile<false>(st[d & 1], t32, lo, hi, a.score_scale, qx, s);
-          else
-            compute_subtile<true>(st[d & 1], t32, lo, hi, a.score_scale, qx, s);
-          if (t32 + kDepth <= twl) it.issue(ring, d, t32 + kDepth);
-        }
-      }
-      tw = twl + 1;
-    }
-    s.bad = it.bad;
+    reset_state(s);
+    seg_run.template stream<KP>(a.score_scale, lo, hi, t_new, upd_b, kcode, vcode, qx, s);
 
     // ---- finish the piece
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) s.acc[t][r] += __shfl_xor(s.acc[t][r], 8, 64);
-    const float lsum = wave_sum_same_g(s.l);
-    const bool bad = __any(s.bad);
-    // dims in lane order: o[4r + tau] = dim 16q + 4r + tau
     float o[16];
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) o[4 * r + t] = s.acc[t][r];
+    float lsum;
+    bool bad;
+    finish_piece(s, o, lsum, bad);
 
     const bool whole = (real_beg >= wbeg) && (real_end <= wend);
     if (whole) {
-      if (e == 0 && g < a.G) {
-        const float f = bad ? NAN : a.v_scale / lsum;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[i] *= f;
-        store_bf16x16(a.out + (static_cast<int64_t>(b) * a.Hq + h * a.G + g) * kHeadDim + 16 * q, o);
-      }
+      store_whole(a, b, h, o, lsum, bad);
     } else if (sc.of(real_end - 1) == sc.of(real_beg) + 1 &&
                sc.of(real_beg) / kWavesPerWG == sc.of(real_end - 1) / kWavesPerWG) {
       // cut once, both pieces in this workgroup: hand off through LDS
@@ -1237,28 +1295,188 @@ __global__ void __launch_bounds__(kThreads, kWGPerCU * kWavesPerWG / 4) decode_a
   wait_vmcnt<0>();  // no direct-to-LDS load outlives the wave
 }
 
+// ---- direct launches ----------------------------------------------------------
+// When no item of a launch can exceed kDirectMax sub-tiles -- every
+// sliding-window launch (a window of up to 224 keys spans at most 8), and
+// full launches whose tables cover at most 256 keys -- items need no
+// balancing: item (b, h) = (i / Hkv, i % Hkv) gets `pieces` waves (1 or 2) of
+// one workgroup straight from its index.  No position scan, no item search:
+// the item's position, its whole table row (the trimmed window table is at
+// most 9 entries wide), its queries and its new token's rows are fetched in
+// one round trip, and the K/V loads go out as soon as the position is known.
+// With two pieces the item splits after its first (nr + 1) / 2 sub-tiles and
+// the two pieces merge through LDS -- the same split and merge as the
+// stream-K kernel's two-waves-per-item mode, so both kernels give identical
+// bits for the same items.
+constexpr int kDirectMax = 8;      // longest item (sub-tiles) of a direct launch
+constexpr int kDirectWGPerCU = 2;  // workgroups per CU the direct kernel is compiled for
+constexpr int kDirectRegs = 1;     // table entries in registers: 64 (a whole direct row)
+
 template <int BK, bool WINDOWED, bool KP, bool ROPE>
-hipError_t launch(const AttnArgs& a, int n_wg, size_t lds, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_attn_kernel<BK, WINDOWED, KP, ROPE>), dim3(n_wg), dim3(kThreads), lds,
-                     stream, a);
+__global__ void __launch_bounds__(kThreads, kDirectWGPerCU * kWavesPerWG / 4)
+    decode_attn_direct_kernel(AttnArgs a, int pieces) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_ring[kWavesPerWG * kDepth * kSlotBytes];
+  __shared__ __attribute__((aligned(16))) float s_part[kWavesPerWG * kSlotFloats];
+  __shared__ int s_cnt[kWavesPerWG / 2];
+  // wave-uniform indices (readfirstlane: the compiler cannot tell that
+  // threadIdx.x >> 6 is uniform, and the buffer descriptors need SGPRs)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = lane_id();
+  const int m = lane & 15, q = lane >> 4, e = m >> 3, g = m & 7;
+  uint8_t* ring = s_ring + wave * (kDepth * kSlotBytes);
+  const int64_t wid = static_cast<int64_t>(blockIdx.x) * kWavesPerWG + wave;
+  const int64_t item = wid / pieces;
+  const int piece = __builtin_amdgcn_readfirstlane(static_cast<int>(wid % pieces));
+  const bool live = item < static_cast<int64_t>(a.B) * a.Hkv;
+  const int b = __builtin_amdgcn_readfirstlane(live ? static_cast<int>(item / a.Hkv) : 0);
+  const int h = __builtin_amdgcn_readfirstlane(live ? static_cast<int>(item % a.Hkv) : 0);
+
+  // ---- set-up loads, none of which depends on the position
+  const int fp = __builtin_amdgcn_readfirstlane(live ? a.frame_pos[b] : -1);
+  Item<BK, WINDOWED, KP, kDirectRegs> it(a, b, h);
+  it.load_window(0);
+  u32x4_t q0 = {0u, 0u, 0u, 0u}, q1 = {0u, 0u, 0u, 0u};
+  if (live && g < a.G) {
+    const uint16_t* qp = a.q + (static_cast<int64_t>(b) * a.Hq + h * a.G + g) * kHeadDim + 16 * q;
+    q0 = *reinterpret_cast<const u32x4_t*>(qp);
+    q1 = *reinterpret_cast<const u32x4_t*>(qp + 8);
+  }
+  f32x4_t rc[4], rs[4];
+  if (ROPE) {
+    const int64_t ro = static_cast<int64_t>(b) * (kHeadDim / 2) + 16 * (q & 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      rc[i] = *reinterpret_cast<const f32x4_t*>(a.rope_cos + ro + 4 * i);
+      rs[i] = *reinterpret_cast<const f32x4_t*>(a.rope_sin + ro + 4 * i);
+    }
+  }
+  uint16_t kn_bits = 0, vn_bits = 0;
+  float kn_c = 1.f, kn_s = 0.f;
+  int64_t upd_b = -1;
+  if (a.k_new != nullptr && live) {
+    const int64_t row = (static_cast<int64_t>(b) * a.Hkv + h) * kHeadDim + lane;
+    kn_bits = a.k_new[row];
+    vn_bits = a.v_new[row];
+    upd_b = a.upd[b];
+    if (ROPE) {
+      const int64_t ci = static_cast<int64_t>(b) * (kHeadDim / 2) + (lane & (kHeadDim / 2 - 1));
+      kn_c = a.rope_cos[ci];
+      kn_s = a.rope_sin[ci];
+    }
+  }
+  if (pieces == 2) {
+    // the pair's LDS arrival counter starts at zero (every wave gets here)
+    if (threadIdx.x < kWavesPerWG / 2) s_cnt[threadIdx.x] = 0;
+    __syncthreads();
+  }
+  if (!live) return;
+
+  int lo = 0;
+  bool invalid;
+  const int nr = seq_subtiles<BK, WINDOWED>(a, fp, &lo, &invalid);
+  if (nr == 0) {
+    // no work: +0 rows for an inactive sequence, NaN for a position beyond
+    // the table; the first piece writes the item's G rows
+    if (piece == 0) {
+      const uint32_t f2 = invalid ? 0x7fc07fc0u : 0u;
+      const int gg = lane >> 3, part = lane & 7;
+      if (gg < a.G)
+        *reinterpret_cast<u32x4_t*>(a.out + (static_cast<int64_t>(b) * a.Hq + h * a.G + gg) *
+                                                kHeadDim + 8 * part) = u32x4_t{f2, f2, f2, f2};
+    }
+    return;
+  }
+  const int hi = fp;
+  it.set_range(lo, hi);
+  const int first = pieces == 2 ? (nr + 1) / 2 : nr;  // sub-tiles of the first piece
+  const int segr = piece == 0 ? first : nr - first;
+  if (segr <= 0) return;  // a one-sub-tile item: the first piece holds it whole
+  const bool split = pieces == 2 && nr - first > 0;
+  const int t0 = lo / kSub + (piece == 0 ? 0 : first);
+  const int tlast = t0 + segr - 1;
+
+  Segment<Item<BK, WINDOWED, KP, kDirectRegs>> sg(it, ring, t0, tlast, it.kEntries);
+  sg.start_run();
+  if (ROPE) rotate_queries(q0, q1, rc, rs, q >= 2);
+  uint32_t qx[4][4];
+  expand_queries(q0, q1, e, qx);
+  const int t_new = (a.k_new != nullptr && hi / kSub >= t0 && hi / kSub <= tlast) ? hi / kSub : -1;
+  uint32_t kcode = 0, vcode = 0;
+  if (t_new >= 0) new_token_codes<ROPE>(a, kn_bits, vn_bits, kn_c, kn_s, kcode, vcode);
+  State s;
+  reset_state(s);
+  sg.template stream<KP>(a.score_scale, lo, hi, t_new, upd_b, kcode, vcode, qx, s);
+  wait_vmcnt<0>();
+
+  float o[16];
+  float lsum;
+  bool bad;
+  finish_piece(s, o, lsum, bad);
+  if (!split) {
+    store_whole(a, b, h, o, lsum, bad);
+    return;
+  }
+  // two pieces: each writes its partial to its wave's LDS slot; the second to
+  // arrive merges them in piece order
+  write_partial_lds(s_part + wave * kSlotFloats, o, s.m, bad ? NAN : lsum, lane);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  int old = 0;
+  if (lane == 0)
+    old = __hip_atomic_fetch_add(s_cnt + (wave >> 1), 1, __ATOMIC_ACQ_REL,
+                                 __HIP_MEMORY_SCOPE_WORKGROUP);
+  old = __builtin_amdgcn_readfirstlane(__shfl(old, 0, 64));
+  if (old == 1) {
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    const int w0 = wave & ~1;
+    merge_item<2>(a, b, h, 2, lane,
+                  LdsPieces{s_part + w0 * kSlotFloats, s_part + (w0 + 1) * kSlotFloats});
+  }
+}
+
+// Grid of a launch: `pieces` > 0 selects the direct kernel (n_wg workgroups,
+// `pieces` waves per item), 0 the stream-K kernel (n_wg workgroups, `lds`
+// bytes of dynamic LDS for the prefix).
+struct Grid {
+  int n_wg;
+  int pieces;
+  size_t lds;
+};
+
+template <int BK, bool WINDOWED, bool KP, bool ROPE>
+hipError_t launch(const AttnArgs& a, const Grid& gr, hipStream_t stream) {
+  if (gr.pieces > 0)
+    hipLaunchKernelGGL((decode_attn_direct_kernel<BK, WINDOWED, KP, ROPE>), dim3(gr.n_wg),
+                       dim3(kThreads), 0, stream, a, gr.pieces);
+  else
+    hipLaunchKernelGGL((decode_attn_kernel<BK, WINDOWED, KP, ROPE>), dim3(gr.n_wg), dim3(kThreads),
+                       gr.lds, stream, a);
   return hipGetLastError();
 }
 
 template <int BK, bool ROPE>
-hipError_t launch_kp(const AttnArgs& a, bool win, bool kp, int n_wg, size_t lds, hipStream_t stream) {
+hipError_t launch_kp(const AttnArgs& a, bool win, bool kp, const Grid& gr, hipStream_t stream) {
   if (kp)
-    return win ? launch<BK, true, true, ROPE>(a, n_wg, lds, stream)
-               : launch<BK, false, true, ROPE>(a, n_wg, lds, stream);
-  return win ? launch<BK, true, false, ROPE>(a, n_wg, lds, stream)
-             : launch<BK, false, false, ROPE>(a, n_wg, lds, stream);
+    return win ? launch<BK, true, true, ROPE>(a, gr, stream)
+               : launch<BK, false, true, ROPE>(a, gr, stream);
+  return win ? launch<BK, true, false, ROPE>(a, gr, stream)
+             : launch<BK, false, false, ROPE>(a, gr, stream);
 }
 
 // The rotary variant is a separate instantiation so that calls without it run
 // the kernel without its code.
 template <int BK>
-hipError_t launch_bk(const AttnArgs& a, bool win, bool kp, int n_wg, size_t lds, hipStream_t stream) {
-  return a.rope_cos != nullptr ? launch_kp<BK, true>(a, win, kp, n_wg, lds, stream)
-                               : launch_kp<BK, false>(a, win, kp, n_wg, lds, stream);
+hipError_t launch_bk(const AttnArgs& a, bool win, bool kp, const Grid& gr, hipStream_t stream) {
+  return a.rope_cos != nullptr ? launch_kp<BK, true>(a, win, kp, gr, stream)
+                               : launch_kp<BK, false>(a, win, kp, gr, stream);
+}
+
+// The most sub-tiles one item of a launch can span: keys lie in frame
+// positions [lo, hi] with hi < table_width * block; a window of W keys can
+// start anywhere inside a sub-tile.
+int64_t longest_item(int block, int table_width, int window) {
+  const int64_t full = (static_cast<int64_t>(table_width) * block + kSub - 1) / kSub;
+  if (window <= 0) return full;
+  return std::min<int64_t>(full, (static_cast<int64_t>(window) + 2 * kSub - 2) / kSub);
 }
 
 }  // namespace
@@ -1331,21 +1549,30 @@ hipError_t launch_decode_attn(const AttnLaunch& L, hipStream_t stream) {
   // of each device is cached; concurrent callers may both query it)
   static std::atomic<int> cu_count[64];
   int dev = 0;
+  int cus = 0;
   if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
-    int cus = cu_count[dev].load(std::memory_order_relaxed);
+    cus = cu_count[dev].load(std::memory_order_relaxed);
     if (!cus && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
       cu_count[dev].store(cus, std::memory_order_relaxed);
     const int resident = cus * kWGPerCU * kWavesPerWG;
     if (resident >= kWavesPerWG && a.n_workers > resident) a.n_workers = resident;
   }
-  const int n_wg = a.n_workers / kWavesPerWG;
-  const size_t lds = static_cast<size_t>(L.B + 1) * sizeof(int);
+  Grid gr{a.n_workers / kWavesPerWG, 0, static_cast<size_t>(L.B + 1) * sizeof(int)};
+  if (longest_item(L.block, L.table_width, L.window) <= kDirectMax) {
+    // direct: two waves per item when twice the items fit in the resident waves
+    const int64_t items = static_cast<int64_t>(L.B) * L.Hkv;
+    const int64_t resident = static_cast<int64_t>(cus > 0 ? cus : 256) * kDirectWGPerCU * kWavesPerWG;
+    gr.pieces = 2 * items <= resident ? 2 : 1;
+    const int64_t wgs = (items * gr.pieces + kWavesPerWG - 1) / kWavesPerWG;
+    if (wgs > INT32_MAX) return hipErrorInvalidValue;
+    gr.n_wg = static_cast<int>(wgs);
+  }
   const bool win = L.window > 0;
   switch (L.block) {
-    case 16: return launch_bk<16>(a, win, L.k_packed != 0, n_wg, lds, stream);
-    case 32: return launch_bk<32>(a, win, L.k_packed != 0, n_wg, lds, stream);
-    case 64: return launch_bk<64>(a, win, L.k_packed != 0, n_wg, lds, stream);
-    case 128: return launch_bk<128>(a, win, L.k_packed != 0, n_wg, lds, stream);
+    case 16: return launch_bk<16>(a, win, L.k_packed != 0, gr, stream);
+    case 32: return launch_bk<32>(a, win, L.k_packed != 0, gr, stream);
+    case 64: return launch_bk<64>(a, win, L.k_packed != 0, gr, stream);
+    case 128: return launch_bk<128>(a, win, L.k_packed != 0, gr, stream);
     default: return hipErrorInvalidValue;
   }
 }

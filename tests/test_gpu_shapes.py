@@ -29,6 +29,13 @@ CASES = [
     # a 3-sub-tile item splits 2 + 1 (register prefix, then LDS prefix)
     ("g8_bk16_b40_L1-70_halves", 16, 2, 16, 40, ("uniform", 1, 70), 3, 16),
     ("g4_bk16_b100_L1-70_halves", 16, 4, 16, 100, ("uniform", 1, 70), 7, 17),
+    # the same short contexts behind tables 1024 tokens wide: the full layer
+    # can no longer bound its items by the table, so it runs the stream-K
+    # kernel (its two-waves-per-item mode and, at 8192 sequences, its LDS
+    # prefix) instead of the direct one
+    ("g8_bk16_b40_L1-70_halves_wide", 16, 2, 16, 40, ("uniform", 1, 70), 3, 16, 1024),
+    ("g4_bk16_b100_L1-70_halves_wide", 16, 4, 16, 100, ("uniform", 1, 70), 7, 17, 1024),
+    ("g8_bk16_b8192_L1-40_wide", 8, 1, 16, 8192, ("uniform", 1, 40), 100, 15, 1024),
 ]
 
 
@@ -50,9 +57,9 @@ def _run(cfg, gpu):
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_shapes_match_oracle(case, gpu):
-    name, hq, hkv, block, batch, ctx, inactive, seed = case
+    name, hq, hkv, block, batch, ctx, inactive, seed = case[:8]
     cfg = Config(name, PAIR, batch, hq, hkv, 64, block, ctx, seed=seed, n_inactive=inactive,
-                 max_ctx=ctx[-1])
+                 max_ctx=case[8] if len(case) > 8 else ctx[-1])
     wl, outs, ref = _run(cfg, gpu)
     for i in range(cfg.layers):
         assert_close(outs[i], ref[i], f"{name} layer {i}")
