@@ -626,6 +626,19 @@ struct SlotPieces {
   }
 };
 
+// Consecutive LDS slots holding pieces 0, 1, ... of one item.
+struct LdsSlots {
+  const float* base;
+  __device__ __forceinline__ void load(int k, int g, int part, float& m, float& l, u32x4_t& o0,
+                                       u32x4_t& o1) const {
+    const float* p = base + k * kSlotFloats;
+    m = p[8 * kHeadDim + g];
+    l = p[8 * kHeadDim + 8 + g];
+    o0 = *reinterpret_cast<const u32x4_t*>(p + g * kHeadDim + 8 * part);
+    o1 = *reinterpret_cast<const u32x4_t*>(p + g * kHeadDim + 8 * part + 4);
+  }
+};
+
 // The two pieces of an item cut once inside one workgroup, in LDS.
 struct LdsPieces {
   const float* p0;
@@ -1296,28 +1309,30 @@ __global__ void __launch_bounds__(kThreads, kWGPerCU * kWavesPerWG / 4) decode_a
 }
 
 // ---- direct launches ----------------------------------------------------------
-// When no item of a launch can exceed kDirectMax sub-tiles -- every
-// sliding-window launch (a window of up to 224 keys spans at most 8), and
-// full launches whose tables cover at most 256 keys -- items need no
-// balancing: item (b, h) = (i / Hkv, i % Hkv) gets `pieces` waves (1 or 2) of
-// one workgroup straight from its index.  No position scan, no item search:
-// the item's position, its whole table row (the trimmed window table is at
-// most 9 entries wide), its queries and its new token's rows are fetched in
-// one round trip, and the K/V loads go out as soon as the position is known.
-// With two pieces the item splits after its first (nr + 1) / 2 sub-tiles and
-// the two pieces merge through LDS -- the same split and merge as the
-// stream-K kernel's two-waves-per-item mode, so both kernels give identical
-// bits for the same items.
-constexpr int kDirectMax = 8;      // longest item (sub-tiles) of a direct launch
-constexpr int kDirectWGPerCU = 2;  // workgroups per CU the direct kernel is compiled for
-constexpr int kDirectRegs = 1;     // table entries in registers: 64 (a whole direct row)
+// When the items of a launch are short enough not to need balancing -- every
+// sliding-window launch (a window of up to 224 keys spans at most 8
+// sub-tiles), full launches whose tables cover at most 8 sub-tiles, and
+// launches of items up to 32 sub-tiles with enough of them to fill the GPU
+// -- item (b, h) = (i / Hkv, i % Hkv) gets `pieces` waves (1, 2 or 4) of one
+// workgroup straight from its index.  No position scan, no item search: the
+// item's position, its first table window, its queries and its new token's
+// rows are fetched in one round trip, and the K/V loads go out as soon as the
+// position is known.  With several pieces the item's nr sub-tiles are split
+// into consecutive parts of nr / pieces (the first nr % pieces parts one
+// more) and the parts merge, in order, through LDS; a two-piece split is the
+// same as the stream-K kernel's two-waves-per-item mode, so both kernels give
+// identical bits for the same items.
+constexpr int kDirectMax = 8;        // longest item (sub-tiles) always run directly
+constexpr int kDirectMaxWide = 32;   // ... and when the items fill the resident waves
+constexpr int kDirectWGPerCU = 2;    // workgroups per CU the direct kernel is compiled for
+constexpr int kDirectRegs = 1;       // table entries in registers: 64 per window
 
 template <int BK, bool WINDOWED, bool KP, bool ROPE>
 __global__ void __launch_bounds__(kThreads, kDirectWGPerCU * kWavesPerWG / 4)
-    decode_attn_direct_kernel(AttnArgs a, int pieces) {
+    decode_attn_direct_kernel(AttnArgs a, int pieces_log2) {
   __shared__ __attribute__((aligned(16))) uint8_t s_ring[kWavesPerWG * kDepth * kSlotBytes];
   __shared__ __attribute__((aligned(16))) float s_part[kWavesPerWG * kSlotFloats];
-  __shared__ int s_cnt[kWavesPerWG / 2];
+  __shared__ int s_cnt[kWavesPerWG];
   // wave-uniform indices (readfirstlane: the compiler cannot tell that
   // threadIdx.x >> 6 is uniform, and the buffer descriptors need SGPRs)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1325,8 +1340,9 @@ __global__ void __launch_bounds__(kThreads, kDirectWGPerCU * kWavesPerWG / 4)
   const int m = lane & 15, q = lane >> 4, e = m >> 3, g = m & 7;
   uint8_t* ring = s_ring + wave * (kDepth * kSlotBytes);
   const int64_t wid = static_cast<int64_t>(blockIdx.x) * kWavesPerWG + wave;
-  const int64_t item = wid / pieces;
-  const int piece = __builtin_amdgcn_readfirstlane(static_cast<int>(wid % pieces));
+  const int pieces = 1 << pieces_log2;  // 1, 2 or 4
+  const int64_t item = wid >> pieces_log2;
+  const int piece = __builtin_amdgcn_readfirstlane(static_cast<int>(wid & (pieces - 1)));
   const bool live = item < static_cast<int64_t>(a.B) * a.Hkv;
   const int b = __builtin_amdgcn_readfirstlane(live ? static_cast<int>(item / a.Hkv) : 0);
   const int h = __builtin_amdgcn_readfirstlane(live ? static_cast<int>(item % a.Hkv) : 0);
@@ -1364,9 +1380,9 @@ __global__ void __launch_bounds__(kThreads, kDirectWGPerCU * kWavesPerWG / 4)
       kn_s = a.rope_sin[ci];
     }
   }
-  if (pieces == 2) {
-    // the pair's LDS arrival counter starts at zero (every wave gets here)
-    if (threadIdx.x < kWavesPerWG / 2) s_cnt[threadIdx.x] = 0;
+  if (pieces > 1) {
+    // the items' LDS arrival counters start at zero (every wave gets here)
+    if (threadIdx.x < kWavesPerWG) s_cnt[threadIdx.x] = 0;
     __syncthreads();
   }
   if (!live) return;
@@ -1388,11 +1404,13 @@ __global__ void __launch_bounds__(kThreads, kDirectWGPerCU * kWavesPerWG / 4)
   }
   const int hi = fp;
   it.set_range(lo, hi);
-  const int first = pieces == 2 ? (nr + 1) / 2 : nr;  // sub-tiles of the first piece
-  const int segr = piece == 0 ? first : nr - first;
-  if (segr <= 0) return;  // a one-sub-tile item: the first piece holds it whole
-  const bool split = pieces == 2 && nr - first > 0;
-  const int t0 = lo / kSub + (piece == 0 ? 0 : first);
+  // this piece's part of the nr sub-tiles; only the first min(pieces, nr)
+  // parts hold any
+  const int each = nr >> pieces_log2, extra = nr & (pieces - 1);
+  const int segr = each + (piece < extra ? 1 : 0);
+  if (segr <= 0) return;
+  const int npieces = min(pieces, nr);
+  const int t0 = lo / kSub + piece * each + min(piece, extra);
   const int tlast = t0 + segr - 1;
 
   Segment<Item<BK, WINDOWED, KP, kDirectRegs>> sg(it, ring, t0, tlast, it.kEntries);
@@ -1412,24 +1430,22 @@ __global__ void __launch_bounds__(kThreads, kDirectWGPerCU * kWavesPerWG / 4)
   float lsum;
   bool bad;
   finish_piece(s, o, lsum, bad);
-  if (!split) {
+  if (npieces == 1) {
     store_whole(a, b, h, o, lsum, bad);
     return;
   }
-  // two pieces: each writes its partial to its wave's LDS slot; the second to
-  // arrive merges them in piece order
+  // several pieces: each writes its partial to its wave's LDS slot; the last
+  // to arrive merges them in piece order (the item's waves are consecutive)
   write_partial_lds(s_part + wave * kSlotFloats, o, s.m, bad ? NAN : lsum, lane);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   int old = 0;
+  const int slot0 = wave - piece;
   if (lane == 0)
-    old = __hip_atomic_fetch_add(s_cnt + (wave >> 1), 1, __ATOMIC_ACQ_REL,
-                                 __HIP_MEMORY_SCOPE_WORKGROUP);
+    old = __hip_atomic_fetch_add(s_cnt + slot0, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
   old = __builtin_amdgcn_readfirstlane(__shfl(old, 0, 64));
-  if (old == 1) {
+  if (old == npieces - 1) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    const int w0 = wave & ~1;
-    merge_item<2>(a, b, h, 2, lane,
-                  LdsPieces{s_part + w0 * kSlotFloats, s_part + (w0 + 1) * kSlotFloats});
+    merge_item<kWavesPerWG>(a, b, h, npieces, lane, LdsSlots{s_part + slot0 * kSlotFloats});
   }
 }
 
@@ -1446,7 +1462,7 @@ template <int BK, bool WINDOWED, bool KP, bool ROPE>
 hipError_t launch(const AttnArgs& a, const Grid& gr, hipStream_t stream) {
   if (gr.pieces > 0)
     hipLaunchKernelGGL((decode_attn_direct_kernel<BK, WINDOWED, KP, ROPE>), dim3(gr.n_wg),
-                       dim3(kThreads), 0, stream, a, gr.pieces);
+                       dim3(kThreads), 0, stream, a, gr.pieces == 4 ? 2 : gr.pieces == 2 ? 1 : 0);
   else
     hipLaunchKernelGGL((decode_attn_kernel<BK, WINDOWED, KP, ROPE>), dim3(gr.n_wg), dim3(kThreads),
                        gr.lds, stream, a);
@@ -1473,6 +1489,20 @@ hipError_t launch_bk(const AttnArgs& a, bool win, bool kp, const Grid& gr, hipSt
 // The most sub-tiles one item of a launch can span: keys lie in frame
 // positions [lo, hi] with hi < table_width * block; a window of W keys can
 // start anywhere inside a sub-tile.
+// Waves per item of a direct launch (0: run the stream-K kernel).  Items of
+// at most kDirectMax sub-tiles always run directly, longer ones up to
+// kDirectMaxWide when the items alone fill at least half the resident waves;
+// an item gets as many pieces (4, 2, 1) as the resident waves hold for every
+// item, but no more than half its sub-tiles.
+int direct_pieces(int64_t batch, int kv_heads, int64_t longest, int cus) {
+  const int64_t items = batch * kv_heads;
+  const int64_t resident = static_cast<int64_t>(cus > 0 ? cus : 256) * kDirectWGPerCU * kWavesPerWG;
+  if (longest > kDirectMaxWide || (longest > kDirectMax && 2 * items < resident)) return 0;
+  for (int p = kWavesPerWG; p > 1; p /= 2)
+    if (p * items <= resident && 2 * p <= longest) return p;
+  return 1;
+}
+
 int64_t longest_item(int block, int table_width, int window) {
   const int64_t full = (static_cast<int64_t>(table_width) * block + kSub - 1) / kSub;
   if (window <= 0) return full;
@@ -1558,11 +1588,9 @@ hipError_t launch_decode_attn(const AttnLaunch& L, hipStream_t stream) {
     if (resident >= kWavesPerWG && a.n_workers > resident) a.n_workers = resident;
   }
   Grid gr{a.n_workers / kWavesPerWG, 0, static_cast<size_t>(L.B + 1) * sizeof(int)};
-  if (longest_item(L.block, L.table_width, L.window) <= kDirectMax) {
-    // direct: two waves per item when twice the items fit in the resident waves
+  gr.pieces = direct_pieces(L.B, L.Hkv, longest_item(L.block, L.table_width, L.window), cus);
+  if (gr.pieces > 0) {
     const int64_t items = static_cast<int64_t>(L.B) * L.Hkv;
-    const int64_t resident = static_cast<int64_t>(cus > 0 ? cus : 256) * kDirectWGPerCU * kWavesPerWG;
-    gr.pieces = 2 * items <= resident ? 2 : 1;
     const int64_t wgs = (items * gr.pieces + kWavesPerWG - 1) / kWavesPerWG;
     if (wgs > INT32_MAX) return hipErrorInvalidValue;
     gr.n_wg = static_cast<int>(wgs);
