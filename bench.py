@@ -225,6 +225,21 @@ def cpu_baseline(wl, bufs_dev, seconds, workers):
             "one_core": one}
 
 
+def full_kernel_name(cfg, wl, args):
+    """Which attention kernel the library launches for this workload's full
+    layers (for the label only; the library decides on the same shapes):
+    the direct kernel when no item can exceed 8 sub-tiles of 32 keys, or 32
+    when the items alone fill half of the GPU's resident waves (256 CUs x 8),
+    else the stream-K kernel."""
+    import math
+    longest = math.ceil(wl.bt_full.shape[1] * cfg.block / 32)
+    items = cfg.batch * cfg.hkv
+    direct = longest <= 8 or (longest <= 32 and 2 * items >= 256 * 8)
+    name = "decode_attn_direct_kernel" if direct else "decode_attn_kernel"
+    return (f"{name}<{cfg.block}, false, {str(args.k_layout == 'packed').lower()}, "
+            f"{str(args.rope).lower()}> (full layers)")
+
+
 def identity_tables(wl):
     """The control run's tables: sequence b's full-table blocks are the pool's
     ids b*W .. b*W + n - 1 (W = table width) and its window blocks follow all
@@ -347,11 +362,16 @@ def main():
                              dev) if has_swa else None
     outs = [torch.empty_like(q[i]) for i in range(cfg.layers)]
     sm = 1.0 / float(np.sqrt(cfg.head_dim))
+    # the layer entry point runs window layers at even and full layers at odd
+    # indices (layer i on buffer i // 2): an alternating schedule maps onto it
+    # as is, a lone full layer as layer 1 (the full layer of buffer 0)
     alternating = all(k == ("swa" if i % 2 == 0 else "full") for i, k in enumerate(cfg.kinds))
+    lone_full = tuple(cfg.kinds) == ("full",)
+    layer_id = (lambda i: i) if alternating else (lambda i: 1)
     kp = args.k_layout == "packed"
     step_desc = P.make_step(bufs, ctl, bt_full, cfg.batch, cfg.hq, cfg.hkv, cfg.head_dim,
                             cfg.block, cfg.window, wl.nb, k_packed=kp,
-                            **rkw) if alternating else None
+                            **rkw) if (alternating or lone_full) else None
 
     def attn(i):
         swa = cfg.kinds[i] == "swa"
@@ -373,8 +393,9 @@ def main():
 
     def layer(i):
         if step_desc is not None:
-            P.pkv_decode_layer(step_desc, i, q[i], k_new[i], v_new[i], wl.k_scale[i],
-                               wl.v_scale[i], sm, outs[i], ws_swa if i % 2 == 0 else ws_full)
+            li = layer_id(i)
+            P.pkv_decode_layer(step_desc, li, q[i], k_new[i], v_new[i], wl.k_scale[i],
+                               wl.v_scale[i], sm, outs[i], ws_swa if li % 2 == 0 else ws_full)
         else:
             update(i)
             attn(i)
@@ -518,7 +539,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": f"decode_attn_kernel<{cfg.block}, false, {str(args.k_layout == 'packed').lower()}, {str(args.rope).lower()}> (full layers)",
+                     "kernel": full_kernel_name(cfg, wl, args),
                      "bytes_per_launch": full_bytes, "avg_launch_us": round(full_us, 2),
                      "swa_avg_launch_us": round(swa_us, 2) if swa_us else None},
         "hbm_ceiling": None,
