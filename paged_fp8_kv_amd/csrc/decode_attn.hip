@@ -1339,13 +1339,17 @@ __global__ void __launch_bounds__(kThreads, kDirectWGPerCU * kWavesPerWG / 4)
   const int lane = lane_id();
   const int m = lane & 15, q = lane >> 4, e = m >> 3, g = m & 7;
   uint8_t* ring = s_ring + wave * (kDepth * kSlotBytes);
-  const int64_t wid = static_cast<int64_t>(blockIdx.x) * kWavesPerWG + wave;
+  // 32-bit indices (the host launches at most INT32_MAX waves): a 64-bit
+  // division by the head count took ~280 scalar instructions ahead of the
+  // first load
+  const uint32_t wid = blockIdx.x * static_cast<uint32_t>(kWavesPerWG) + wave;
   const int pieces = 1 << pieces_log2;  // 1, 2 or 4
-  const int64_t item = wid >> pieces_log2;
+  const uint32_t item = wid >> pieces_log2;
   const int piece = __builtin_amdgcn_readfirstlane(static_cast<int>(wid & (pieces - 1)));
-  const bool live = item < static_cast<int64_t>(a.B) * a.Hkv;
-  const int b = __builtin_amdgcn_readfirstlane(live ? static_cast<int>(item / a.Hkv) : 0);
-  const int h = __builtin_amdgcn_readfirstlane(live ? static_cast<int>(item % a.Hkv) : 0);
+  const uint32_t hkv = static_cast<uint32_t>(a.Hkv);
+  const bool live = item < static_cast<uint32_t>(a.B) * hkv;
+  const int b = __builtin_amdgcn_readfirstlane(live ? static_cast<int>(item / hkv) : 0);
+  const int h = __builtin_amdgcn_readfirstlane(live ? static_cast<int>(item - b * hkv) : 0);
 
   // ---- set-up loads, none of which depends on the position
   const int fp = __builtin_amdgcn_readfirstlane(live ? a.frame_pos[b] : -1);
@@ -1591,9 +1595,9 @@ hipError_t launch_decode_attn(const AttnLaunch& L, hipStream_t stream) {
   gr.pieces = direct_pieces(L.B, L.Hkv, longest_item(L.block, L.table_width, L.window), cus);
   if (gr.pieces > 0) {
     const int64_t items = static_cast<int64_t>(L.B) * L.Hkv;
-    const int64_t wgs = (items * gr.pieces + kWavesPerWG - 1) / kWavesPerWG;
-    if (wgs > INT32_MAX) return hipErrorInvalidValue;
-    gr.n_wg = static_cast<int>(wgs);
+    // the kernel indexes waves in 32 bits
+    if (items * gr.pieces > INT32_MAX) return hipErrorInvalidValue;
+    gr.n_wg = static_cast<int>((items * gr.pieces + kWavesPerWG - 1) / kWavesPerWG);
   }
   const bool win = L.window > 0;
   switch (L.block) {
