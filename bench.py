@@ -477,28 +477,32 @@ def main():
     # ---- dominant kernel: the full-layer launches of a step, made exactly as the
     # step makes them but back to back between two events on their stream (the
     # layers of a step are independent), so the average is the launch duration
-    # plus the gap between consecutive launches; the same for the window layers
+    # plus the gap between consecutive launches; the same for the window layers,
+    # issued right behind the full ones so that the device is still busy when
+    # they are queued.  A group of fewer than 16 launches is issued several
+    # times over, so that the queue stays ahead of the device and the host's
+    # launch overhead does not land between the launches.
     full_layers = [i for i, k in enumerate(cfg.kinds) if k == "full"]
     swa_layers = [i for i, k in enumerate(cfg.kinds) if k == "swa"]
-    ev = []
-    ev_swa = []
-    n_ev_steps = max(1, min(args.steps, 5))
+    ev = {"full": [], "swa": []}
     torch.cuda.synchronize()
-    for _ in range(n_ev_steps):
+    for _ in range(max(1, min(args.steps, 5))):
         setup()
-        for group, sink in ((full_layers, ev), (swa_layers, ev_swa)):
+        for name, group in (("full", full_layers), ("swa", swa_layers)):
             if not group:
                 continue
+            reps = max(1, -(-16 // len(group)))
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
             a.record()
-            for i in group:
-                layer(i)
+            for _ in range(reps):
+                for i in group:
+                    layer(i)
             b.record()
-            sink.append((a, b, len(group)))
+            ev[name].append((a, b, reps * len(group)))
     torch.cuda.synchronize()
-    full_us = float(np.mean([a.elapsed_time(b) / n for a, b, n in ev])) * 1e3
-    swa_us = float(np.mean([a.elapsed_time(b) / n for a, b, n in ev_swa])) * 1e3 if ev_swa else None
+    full_us = float(np.mean([a.elapsed_time(b) / n for a, b, n in ev["full"]])) * 1e3
+    swa_us = float(np.mean([a.elapsed_time(b) / n for a, b, n in ev["swa"]])) * 1e3 if ev["swa"] else None
     for a, b in zip(outs, ref):
         assert torch.equal(a, b), "outputs changed between steps"
 
