@@ -60,11 +60,13 @@ constexpr int kDepth = PKV_DEPTH;
 constexpr int kTinyItem = 8;          // items this short (sub-tiles) are never split
 // Fixed cost of starting a short item (shorter than a share), in sub-tiles:
 // the wait for its set-up loads and first K/V loads plus the fill and drain
-// of the ring (about 2.4 us, measured, against 0.6 us per streamed sub-tile).
-// The static split of full-attention launches counts it on top of the
-// item's sub-tiles so that waves given many short items are not the last to
-// finish (window items are all short and alike: they are not weighted).
-constexpr int kItemCost = 4;
+// of the ring.  Per-wave timelines of a ragged batch (128 sequences, 128 to
+// 32768 tokens) fit 0.63 us per streamed sub-tile and 3.5-3.8 us per item,
+// about 6 sub-tiles; with 4, the waves given 10-13 short items finished
+// 10-15 us after the median one.  The static split of full-attention
+// launches counts it on top of the item's sub-tiles (window items are all
+// short and alike: they are not weighted).
+constexpr int kItemCost = 6;
 // Waves per SIMD the kernel is compiled for (= workgroups per CU, 4 waves
 // each); the stream-K shares assume every worker is resident at once.
 #ifndef PKV_WG_PER_CU
