@@ -479,27 +479,49 @@ def main():
     # layers of a step are independent), so the average is the launch duration
     # plus the gap between consecutive launches; the same for the window layers,
     # issued right behind the full ones so that the device is still busy when
-    # they are queued.  A group of fewer than 16 launches is issued several
-    # times over, so that the queue stays ahead of the device and the host's
-    # launch overhead does not land between the launches.
+    # they are queued.  The host needs about 7 us to issue a launch: a group of
+    # launches shorter than that would be timed with the host's gaps, so short
+    # groups are issued 16 times over between their events.  Long launches are
+    # not repeated: after a few milliseconds of back-to-back full layers the
+    # same launch was measured up to 25% slower (the device's clocks drop
+    # under sustained load).  When a step has fewer than 4 full layers, a
+    # first timed pass decides whether they are short, and each timed group is
+    # preceded by an untimed pass so that the host's first launch is queued
+    # while the device is busy.
     full_layers = [i for i, k in enumerate(cfg.kinds) if k == "full"]
     swa_layers = [i for i, k in enumerate(cfg.kinds) if k == "swa"]
     ev = {"full": [], "swa": []}
+
+    def timed(group, reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            for i in group:
+                layer(i)
+        b.record()
+        return a, b
+
     torch.cuda.synchronize()
+    reps_full = 1
+    if 0 < len(full_layers) < 4:
+        setup()
+        la, lb = timed(full_layers, 1)
+        lb.synchronize()
+        if la.elapsed_time(lb) * 1e3 / len(full_layers) < 60.0:
+            reps_full = -(-16 // len(full_layers))
     for _ in range(max(1, min(args.steps, 5))):
         setup()
-        for name, group in (("full", full_layers), ("swa", swa_layers)):
-            if not group:
-                continue
-            reps = max(1, -(-16 // len(group)))
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record()
-            for _ in range(reps):
-                for i in group:
-                    layer(i)
-            b.record()
-            ev[name].append((a, b, reps * len(group)))
+        if 0 < len(full_layers) < 4:
+            for i in full_layers:  # untimed: the queue stays ahead of the device
+                layer(i)
+        if full_layers:
+            a, b = timed(full_layers, reps_full)
+            ev["full"].append((a, b, reps_full * len(full_layers)))
+        if swa_layers:
+            reps = -(-16 // len(swa_layers))
+            a, b = timed(swa_layers, reps)
+            ev["swa"].append((a, b, reps * len(swa_layers)))
     torch.cuda.synchronize()
     full_us = float(np.mean([a.elapsed_time(b) / n for a, b, n in ev["full"]])) * 1e3
     swa_us = float(np.mean([a.elapsed_time(b) / n for a, b, n in ev["swa"]])) * 1e3 if ev["swa"] else None
