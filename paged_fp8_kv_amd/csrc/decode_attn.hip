@@ -436,10 +436,12 @@ __device__ __forceinline__ void patch_slot(uint8_t* ring, int slot, int tok, uin
 // One 32-token sub-tile: scores, online-softmax update and PV accumulation.
 // MASKED selects the edge path (keys outside [lo, hi] removed); the stage
 // registers are never written here, so the interior path carries no copies.
-template <bool MASKED>
+// LO: the queries are carried as bf16 pairs hi + lo (rotated queries): the
+// scores take a second pass of MFMAs over the low parts, with the same K.
+template <bool MASKED, bool LO = false>
 __device__ __forceinline__ void compute_subtile(const Stage& st, int t32, int lo, int hi,
                                                 float score_scale, const uint32_t (&qx)[4][4],
-                                                State& s) {
+                                                const uint32_t (&qxl)[4][4], State& s) {
   const int lane = lane_id();
   const int m = lane & 15, q = lane >> 4, e = m >> 3;
   const int base = t32 * kSub;
@@ -470,6 +472,10 @@ __device__ __forceinline__ void compute_subtile(const Stage& st, int t32, int lo
     bf16x8_t A = __builtin_bit_cast(bf16x8_t, av);
     bf16x8_t Bq = __builtin_bit_cast(bf16x8_t, qx[i]);
     sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bq, sacc, 0, 0, 0);
+    if constexpr (LO) {
+      bf16x8_t Bl = __builtin_bit_cast(bf16x8_t, qxl[i]);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bl, sacc, 0, 0, 0);
+    }
   }
   // lane holds scores of query g for tokens base + 8q + 2r + e
   float x[4];
@@ -761,29 +767,37 @@ __device__ __forceinline__ int64_t first_item_start_at_or_after(const Pre& pre, 
 }
 
 // Half-split rotation of the lane's 16 query dims (16q .. 16q+15, packed bf16
-// in q0, q1); the partner dims 16(q^2) .. live in lane ^ 32.  fp32, then
-// rounded to bf16 for the score MFMA.
-__device__ __forceinline__ void rotate_queries(u32x4_t& q0, u32x4_t& q1, const f32x4_t (&c)[4],
-                                               const f32x4_t (&s)[4], bool upper) {
+// in q0, q1); the partner dims 16(q^2) .. live in lane ^ 32.  In fp32, then
+// carried as two bf16 parts: q0, q1 get the rounded value and l0, l1 what
+// that rounding left out (exact in fp32, rounded to bf16 in turn), so that
+// the scores see about 16 significant bits of each rotated dim.
+__device__ __forceinline__ void rotate_queries(u32x4_t& q0, u32x4_t& q1, u32x4_t& l0, u32x4_t& l1,
+                                               const f32x4_t (&c)[4], const f32x4_t (&s)[4],
+                                               bool upper) {
   uint32_t w[8] = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
   uint32_t p[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) p[k] = static_cast<uint32_t>(__shfl_xor(static_cast<int>(w[k]), 32));
-  uint32_t r[8];
+  uint32_t r[8], rl[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    uint32_t lohi[2];
+    uint32_t hh[2], ll[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int d = 2 * k + e;
       const float x = __uint_as_float((e ? w[k] & 0xffff0000u : w[k] << 16));
       const float xp = __uint_as_float((e ? p[k] & 0xffff0000u : p[k] << 16));
-      lohi[e] = f32_to_bf16_bits(rope_turn(x, xp, c[d >> 2][d & 3], s[d >> 2][d & 3], upper));
+      const float y = rope_turn(x, xp, c[d >> 2][d & 3], s[d >> 2][d & 3], upper);
+      hh[e] = f32_to_bf16_bits(y);
+      ll[e] = f32_to_bf16_bits(y - bf16_bits_to_f32(static_cast<uint16_t>(hh[e])));
     }
-    r[k] = lohi[0] | (lohi[1] << 16);
+    r[k] = hh[0] | (hh[1] << 16);
+    rl[k] = ll[0] | (ll[1] << 16);
   }
   q0 = u32x4_t{r[0], r[1], r[2], r[3]};
   q1 = u32x4_t{r[4], r[5], r[6], r[7]};
+  l0 = u32x4_t{rl[0], rl[1], rl[2], rl[3]};
+  l1 = u32x4_t{rl[4], rl[5], rl[6], rl[7]};
 }
 
 // Expanded queries for the score MFMA: qx[i][k] holds q[g][16q + 4i + k]
@@ -855,10 +869,11 @@ struct Segment {
 
   // The first run must have been started.  t_new: the sub-tile holding the
   // new token (its codes patched into the slot before it is read), or -1.
-  template <bool KP>
+  template <bool KP, bool LO = false>
   __device__ __forceinline__ void stream(float score_scale, int lo, int hi, int t_new,
                                          int64_t upd, uint32_t kcode, uint32_t vcode,
-                                         const uint32_t (&qx)[4][4], State& s) {
+                                         const uint32_t (&qx)[4][4], const uint32_t (&qxl)[4][4],
+                                         State& s) {
     for (bool first = true; tw <= tlast; first = false) {
       if (!first) start_run();
       Stage st[2];
@@ -879,9 +894,9 @@ struct Segment {
             read_slot<KP>(ring, (d + 1) % kDepth, st[(d + 1) & 1]);
           }
           if (t32 * kSub >= lo && t32 * kSub + kSub - 1 <= hi)
-            compute_subtile<false>(st[d & 1], t32, lo, hi, score_scale, qx, s);
+            compute_subtile<false, LO>(st[d & 1], t32, lo, hi, score_scale, qx, qxl, s);
           else
-            compute_subtile<true>(st[d & 1], t32, lo, hi, score_scale, qx, s);
+            compute_subtile<true, LO>(st[d & 1], t32, lo, hi, score_scale, qx, qxl, s);
           if (t32 + kDepth <= twl) it.issue(ring, d, t32 + kDepth);
         }
       }
@@ -1037,8 +1052,12 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const Pre& s_pr
     // or the new token's rows, so those loads overlap the ring fill
     seg_run.start_run();
 
-    if (rope) rotate_queries(q0, q1, rc, rs, q >= 2);
-    uint32_t qx[4][4];
+    uint32_t qx[4][4], qxl[4][4];
+    if (rope) {
+      u32x4_t l0, l1;
+      rotate_queries(q0, q1, l0, l1, rc, rs, q >= 2);
+      expand_queries(l0, l1, e, qxl);
+    }
     expand_queries(q0, q1, e, qx);
 
     // The new token (frame position hi) is in sub-tile t_new; with a fused
@@ -1051,7 +1070,10 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const Pre& s_pr
     if (t_new >= 0) new_token_codes<ROPE>(a, kn_bits, vn_bits, kn_c, kn_s, kcode, vcode);
     State s;
     reset_state(s);
-    seg_run.template stream<KP>(a.score_scale, lo, hi, t_new, upd_b, kcode, vcode, qx, s);
+    if constexpr (ROPE)
+      seg_run.template stream<KP, true>(a.score_scale, lo, hi, t_new, upd_b, kcode, vcode, qx, qxl, s);
+    else
+      seg_run.template stream<KP>(a.score_scale, lo, hi, t_new, upd_b, kcode, vcode, qx, qx, s);
 
     // ---- finish the piece
     float o[16];
@@ -1421,15 +1443,22 @@ __global__ void __launch_bounds__(kThreads, kDirectWGPerCU * kWavesPerWG / 4)
 
   Segment<Item<BK, WINDOWED, KP, kDirectRegs>> sg(it, ring, t0, tlast, it.kEntries);
   sg.start_run();
-  if (ROPE) rotate_queries(q0, q1, rc, rs, q >= 2);
-  uint32_t qx[4][4];
+  uint32_t qx[4][4], qxl[4][4];
+  if (ROPE) {
+    u32x4_t l0, l1;
+    rotate_queries(q0, q1, l0, l1, rc, rs, q >= 2);
+    expand_queries(l0, l1, e, qxl);
+  }
   expand_queries(q0, q1, e, qx);
   const int t_new = (a.k_new != nullptr && hi / kSub >= t0 && hi / kSub <= tlast) ? hi / kSub : -1;
   uint32_t kcode = 0, vcode = 0;
   if (t_new >= 0) new_token_codes<ROPE>(a, kn_bits, vn_bits, kn_c, kn_s, kcode, vcode);
   State s;
   reset_state(s);
-  sg.template stream<KP>(a.score_scale, lo, hi, t_new, upd_b, kcode, vcode, qx, s);
+  if constexpr (ROPE)
+    sg.template stream<KP, true>(a.score_scale, lo, hi, t_new, upd_b, kcode, vcode, qx, qxl, s);
+  else
+    sg.template stream<KP>(a.score_scale, lo, hi, t_new, upd_b, kcode, vcode, qx, qx, s);
   wait_vmcnt<0>();
 
   float o[16];

@@ -30,12 +30,11 @@ ATOL, RTOL = 2e-3, 1e-2
 # layers of the full sizes): at most 0.46 ulp beyond the floor, relative L2
 # 1.63e-3 .. 1.68e-3.
 ULP_GUARD, FLOOR_GUARD, L2_GUARD = 1.0, 2.0 ** -11, 2.5e-3
-# With rotary embedding the turned query is rounded to bf16 for the score
-# product (its float64 value in the oracle): scores move by about 1e-3, and
-# outputs by up to about 2.5e-3 absolute wherever the weights shift between
-# keys, so no element-wise bound tighter than the tolerance holds; the
-# aggregate guard stays (measured: relative L2 up to 2.7e-3).
-ROPE_GUARDS = dict(ulp_guard=None, l2_guard=4e-3)
+# With rotary embedding the kernel carries the turned query as a bf16 pair
+# (the rounded value and what the rounding left out) into two score products,
+# about 16 significant bits against the oracle's float64: the same guards
+# hold (measured: at most 0.43 ulp beyond the floor, relative L2 1.68e-3).
+ROPE_GUARDS = dict(ulp_guard=ULP_GUARD, l2_guard=L2_GUARD)
 STATS = []   # (what, max abs err, max err in ulps beyond the floor, relative L2, max ulps)
 
 
