@@ -1521,23 +1521,28 @@ hipError_t launch_bk(const AttnArgs& a, bool win, bool kp, const Grid& gr, hipSt
                                : launch_kp<BK, false>(a, win, kp, gr, stream);
 }
 
-// The most sub-tiles one item of a launch can span: keys lie in frame
-// positions [lo, hi] with hi < table_width * block; a window of W keys can
-// start anywhere inside a sub-tile.
 // Waves per item of a direct launch (0: run the stream-K kernel).  Items of
 // at most kDirectMax sub-tiles always run directly, longer ones up to
-// kDirectMaxWide when the items alone fill at least half the resident waves;
-// an item gets as many pieces (4, 2, 1) as the resident waves hold for every
-// item, but no more than half its sub-tiles.
+// kDirectMaxWide when the items alone fill at least half the resident waves.
+// An item gets as many pieces (4, 2, 1) as the resident waves hold for every
+// item, but no more than half its sub-tiles -- or, while the launch stays at
+// one wave per SIMD, no more than its sub-tiles (a window item of 4-5
+// sub-tiles in four pieces: an 8-sequence window launch 5.93 -> 5.41 us; at
+// two waves per SIMD the same split was slower, 6.31 -> 6.46 us for 64
+// sequences).
 int direct_pieces(int64_t batch, int kv_heads, int64_t longest, int cus) {
   const int64_t items = batch * kv_heads;
+  const int64_t one_per_simd = static_cast<int64_t>(cus > 0 ? cus : 256) * 4;  // four SIMDs per CU
   const int64_t resident = static_cast<int64_t>(cus > 0 ? cus : 256) * kDirectWGPerCU * kWavesPerWG;
   if (longest > kDirectMaxWide || (longest > kDirectMax && 2 * items < resident)) return 0;
   for (int p = kWavesPerWG; p > 1; p /= 2)
-    if (p * items <= resident && 2 * p <= longest) return p;
+    if (p * items <= resident && (2 * p <= longest || (p <= longest && p * items <= one_per_simd))) return p;
   return 1;
 }
 
+// The most sub-tiles one item of a launch can span: keys lie in frame
+// positions [lo, hi] with hi < table_width * block; a window of W keys can
+// start anywhere inside a sub-tile.
 int64_t longest_item(int block, int table_width, int window) {
   const int64_t full = (static_cast<int64_t>(table_width) * block + kSub - 1) / kSub;
   if (window <= 0) return full;
