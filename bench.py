@@ -288,8 +288,10 @@ def main():
                     help="identity: every sequence's blocks consecutive in the pool (isolates "
                          "the cost of the gather)")
     ap.add_argument("--cold-steps", type=int, default=10,
-                    help="steps timed one by one after overwriting 1 GiB (flushes the "
-                         "256 MB Infinity Cache); 0 = none")
+                    help="steps timed one by one after evicting the 256 MB Infinity Cache: this "
+                         "many after writing and reading back 1 GiB (cold_step_ms_median) "
+                         "and as many after only writing it (cold_dirty_step_ms_median); "
+                         "0 = none")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -459,19 +461,27 @@ def main():
     ms = dt * 1e3 / args.steps
     per_step = np.array([marks[k].elapsed_time(marks[k + 1]) for k in range(args.steps)])
 
-    # ---- cold steps: each after overwriting 1 GiB, which evicts the Infinity Cache
-    cold = []
+    # ---- cold steps: each after evicting the 256 MB Infinity Cache with 1 GiB of
+    # other data.  `cold`: the 1 GiB is written and then read back, so that the
+    # caches hold clean unrelated lines when the step starts (as after the
+    # weight reads of a model's other layers).  `cold_dirty`: written only; the
+    # step then also pays for writing back the dirty lines it evicts (≈ 40 us
+    # more at config 3)
+    cold, cold_dirty = [], []
     if args.cold_steps > 0:
         scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        for k in range(args.cold_steps):
+        for k in range(2 * args.cold_steps):
+            clean = k % 2 == 0
             scratch.fill_(k & 0xff)
+            if clean:
+                scratch.view(torch.int64).sum()
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
             a.record()
             g.replay() if use_graph else step()
             b.record()
             torch.cuda.synchronize()
-            cold.append(a.elapsed_time(b))
+            (cold if clean else cold_dirty).append(a.elapsed_time(b))
         del scratch
 
     # ---- dominant kernel: the full-layer launches of a step, made exactly as the
@@ -562,6 +572,7 @@ def main():
         "tokens_per_s": round(cfg.batch / (ms * 1e-3), 1),
         "step_ms_p10_p50_p90": [round(float(np.percentile(per_step, p)), 4) for p in (10, 50, 90)],
         "cold_step_ms_median": round(float(np.median(cold)), 4) if cold else None,
+        "cold_dirty_step_ms_median": round(float(np.median(cold_dirty)), 4) if cold_dirty else None,
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
         "kv_bytes_per_step": step_bytes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
