@@ -159,17 +159,42 @@ __device__ __forceinline__ void wait_vm_stores() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Lane exchanges for the reductions over the lanes of one query (lanes
+// i, i^8, i^16, i^32), done on the VALU instead of through the LDS crossbar
+// (ds_bpermute): xor 8 is a rotation by 8 inside each row of 16 lanes (DPP
+// row_ror:8); for xor 16 and xor 32, v_permlane16_swap / v_permlane32_swap of
+// a value with itself leave each lane its own value in one result and its
+// partner's in the other, so combining the two results is the same
+// commutative max or sum a lane would form with its partner's value.
+__device__ __forceinline__ float dpp_xor8(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float max_with_xor16(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float max_with_xor32(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float sum_with_xor16(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float sum_with_xor32(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
 __device__ __forceinline__ float wave_max_same_g(float v) {
-  v = fmaxf(v, __shfl_xor(v, 8, 64));
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  v = fmaxf(v, __shfl_xor(v, 32, 64));
-  return v;
+  v = fmaxf(v, dpp_xor8(v));
+  v = max_with_xor16(v);
+  return max_with_xor32(v);
 }
 __device__ __forceinline__ float wave_sum_same_g(float v) {
-  v += __shfl_xor(v, 8, 64);
-  v += __shfl_xor(v, 16, 64);
-  v += __shfl_xor(v, 32, 64);
-  return v;
+  v += dpp_xor8(v);
+  v = sum_with_xor16(v);
+  return sum_with_xor32(v);
 }
 
 // Running state of one wave for one item (per lane: query g = m%8, parity e = m/8).
@@ -913,7 +938,7 @@ __device__ __forceinline__ void finish_piece(State& s, float (&o)[16], float& ls
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) s.acc[t][r] += __shfl_xor(s.acc[t][r], 8, 64);
+    for (int r = 0; r < 4; ++r) s.acc[t][r] += dpp_xor8(s.acc[t][r]);
   lsum = wave_sum_same_g(s.l);
   bad = __any(s.bad);
 #pragma unroll
@@ -1480,7 +1505,12 @@ __global__ void __launch_bounds__(kThreads, kDirectWGPerCU * kWavesPerWG / 4)
   old = __builtin_amdgcn_readfirstlane(__shfl(old, 0, 64));
   if (old == npieces - 1) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    merge_item<kWavesPerWG>(a, b, h, npieces, lane, LdsSlots{s_part + slot0 * kSlotFloats});
+    // two pieces in one round of two (the same operations, in the same order,
+    // as a round of four over two pieces)
+    if (npieces == 2)
+      merge_item<2>(a, b, h, 2, lane, LdsSlots{s_part + slot0 * kSlotFloats});
+    else
+      merge_item<kWavesPerWG>(a, b, h, npieces, lane, LdsSlots{s_part + slot0 * kSlotFloats});
   }
 }
 
