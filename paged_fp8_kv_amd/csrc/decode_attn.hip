@@ -118,6 +118,47 @@ __device__ __forceinline__ int seq_subtiles(const AttnArgs& a, int fp, int* lo_o
   return fp / kSub - lo / kSub + 1;
 }
 
+// Integer prefix and reductions over a wave's 64 lanes on the VALU (DPP row
+// shifts and rotations, the gfx950 row-pair and half-wave swaps, lane reads)
+// instead of LDS-crossbar permutes; integer sums and maxima are exact, so the
+// order of the combining steps does not matter.  Every lane of the wave must
+// be active.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int x) {
+  // lanes whose source lies outside their row of 16 read 0
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xf, 0xf, false);
+}
+__device__ __forceinline__ int wave_inclusive_sum(int x) {
+  x += dpp_i32<0x111>(x);  // row_shr:1 -- lane i adds lane i-1 of its row
+  x += dpp_i32<0x112>(x);  // row_shr:2
+  x += dpp_i32<0x114>(x);  // row_shr:4
+  x += dpp_i32<0x118>(x);  // row_shr:8 -- now the prefix within the row
+  const int r = lane_id() >> 4;
+  const int t0 = __builtin_amdgcn_readlane(x, 15), t1 = __builtin_amdgcn_readlane(x, 31),
+            t2 = __builtin_amdgcn_readlane(x, 47);
+  return x + (r > 0 ? t0 : 0) + (r > 1 ? t1 : 0) + (r > 2 ? t2 : 0);
+}
+__device__ __forceinline__ int wave_max_i32(int x) {
+  x = max(x, dpp_i32<0x121>(x));  // row_ror:1
+  x = max(x, dpp_i32<0x122>(x));  // row_ror:2
+  x = max(x, dpp_i32<0x124>(x));  // row_ror:4
+  x = max(x, dpp_i32<0x128>(x));  // row_ror:8 -- the row's maximum in every lane
+  const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = max(static_cast<int>(p[0]), static_cast<int>(p[1]));
+  const auto q = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return max(static_cast<int>(q[0]), static_cast<int>(q[1]));
+}
+__device__ __forceinline__ int wave_sum_i32(int x) {
+  x += dpp_i32<0x121>(x);
+  x += dpp_i32<0x122>(x);
+  x += dpp_i32<0x124>(x);
+  x += dpp_i32<0x128>(x);
+  const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = static_cast<int>(p[0]) + static_cast<int>(p[1]);
+  const auto q = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return static_cast<int>(q[0]) + static_cast<int>(q[1]);
+}
+
 __device__ __forceinline__ void block_exclusive_scan(int* s, int n) {
   __shared__ int wsum[kWavesPerWG];
   const int tid = threadIdx.x;
@@ -127,12 +168,7 @@ __device__ __forceinline__ void block_exclusive_scan(int* s, int n) {
   int local = 0;
   for (int i = beg; i < end; ++i) local += s[i];
   const int lane = tid & 63;
-  int x = local;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
+  const int x = wave_inclusive_sum(local);
   if (lane == 63) wsum[tid >> 6] = x;
   __syncthreads();
   int wave_off = 0;
@@ -1121,7 +1157,7 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const Pre& s_pr
       if (lane == 0)
         old = __hip_atomic_fetch_add(wg.cnt + cf % kWavesPerWG, 1, __ATOMIC_ACQ_REL,
                                      __HIP_MEMORY_SCOPE_WORKGROUP);
-      old = __builtin_amdgcn_readfirstlane(__shfl(old, 0, 64));
+      old = __builtin_amdgcn_readlane(old, 0);
       if (old == 1) {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
         merge_item<2>(a, b, h, 2, lane,
@@ -1136,7 +1172,7 @@ __device__ __forceinline__ void process_chunk(const AttnArgs& a, const Pre& s_pr
       int old = 0;
       int32_t* ctr = a.counters + static_cast<int64_t>(b) * a.Hkv + h;
       if (lane == 0) old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      old = __builtin_amdgcn_readfirstlane(__shfl(old, 0, 64));
+      old = __builtin_amdgcn_readlane(old, 0);
       const int ncontrib = cl - cf + 1;
       if (old == ncontrib - 1) {
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -1243,16 +1279,9 @@ __global__ void __launch_bounds__(kThreads, kWGPerCU * kWavesPerWG / 4) decode_a
       posv = a.frame_pos[lane];
       n = seq_subtiles<BK, WINDOWED>(a, posv, &lo, &inv);
     }
-    int x = n;  // inclusive prefix over the lanes
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int y = __shfl_up(x, off, kWave);
-      if (lane >= off) x += y;
-    }
-    int longest = n;  // in real sub-tiles: decides whether items may be cut
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) longest = max(longest, __shfl_xor(longest, off));
-    longest = __builtin_amdgcn_readfirstlane(longest);
+    const int x = wave_inclusive_sum(n);  // inclusive prefix over the lanes
+    // in real sub-tiles: decides whether items may be cut
+    const int longest = __builtin_amdgcn_readfirstlane(wave_max_i32(n));
     const uint64_t am = __ballot(n > 0);  // sequences with work
     const int64_t items = static_cast<int64_t>(__popcll(am)) * a.Hkv;
     int64_t per_r = 0;
@@ -1276,14 +1305,7 @@ __global__ void __launch_bounds__(kThreads, kWGPerCU * kWavesPerWG / 4) decode_a
         rescan = true;
       }
     }
-    if (rescan) {
-      xv = v;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const int y = __shfl_up(xv, off, kWave);
-        if (lane >= off) xv += y;
-      }
-    }
+    if (rescan) xv = wave_inclusive_sum(v);
     const PreReg pre{xv - v, __builtin_amdgcn_readlane(xv, kWave - 1), posv};
     run_shares<BK, WINDOWED, KP, ROPE>(a, pre, B, longest, ring, wg, per_r, half);
   } else {
@@ -1322,11 +1344,8 @@ __global__ void __launch_bounds__(kThreads, kWGPerCU * kWavesPerWG / 4) decode_a
     }
     // one LDS atomic per wave and quantity (64 lanes on one address would
     // serialise)
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      longest = max(longest, __shfl_xor(longest, off));
-      active += __shfl_xor(active, off);
-    }
+    longest = wave_max_i32(longest);
+    active = wave_sum_i32(active);
     if ((tid & 63) == 0) {
       atomicMax(&s_longest, longest);
       atomicAdd(&s_active, active);
@@ -1502,7 +1521,7 @@ __global__ void __launch_bounds__(kThreads, kDirectWGPerCU * kWavesPerWG / 4)
   const int slot0 = wave - piece;
   if (lane == 0)
     old = __hip_atomic_fetch_add(s_cnt + slot0, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
-  old = __builtin_amdgcn_readfirstlane(__shfl(old, 0, 64));
+  old = __builtin_amdgcn_readlane(old, 0);
   if (old == npieces - 1) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     // two pieces in one round of two (the same operations, in the same order,
