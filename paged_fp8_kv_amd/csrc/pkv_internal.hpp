@@ -9,9 +9,10 @@ namespace pkv {
 constexpr int kHeadDimSupported = 64;   // the only head size the kernels are built for
 constexpr int kMaxWorkers = 4096;          // waves of one attention launch (16 per CU on 256 CUs)
 // 32-token sub-tiles per worker at least: smaller shares only add partials
-// (an 8-sequence batch of 1024-4096 tokens: 20.6 us with 8, 19.9 us with 16,
-// 24.1 us with 32 per full-attention launch)
-constexpr int kMinSubtilesPerWorker = 16;
+// (an 8-sequence batch of 1024-4096 tokens, full-attention launch: 18.7-18.9 us
+// with 10, 18.1-18.3 us with 12, 18.3-18.6 us with 14, 18.5-18.8 us with 16,
+// 20.0 us with 20, 20.8 us with 24)
+constexpr int kMinSubtilesPerWorker = 12;
 constexpr int kMaxBatch = 8192;            // per-sequence prefix scan lives in LDS
 
 struct AttnLaunch {
