@@ -2,8 +2,9 @@
 configurations leave out: query/KV group sizes 1, 2, 4 and 8, blocks of 16,
 64 and 128 tokens, batches on both sides of the 64-sequence register prefix
 up to the largest supported batch, contexts of one token, contexts that end
-mid-block or just past the window, tiny items split between two waves,
-inactive rows and an all-inactive batch.
+mid-block or just past the window, contexts of up to 131,072 tokens (items
+cut into hundreds of pieces), tiny items split between two waves, inactive
+rows and an all-inactive batch.
 Each case runs the alternating window/full layer pair through the layer entry
 point; the written cache is compared byte for byte, the outputs within the
 attention tolerance."""
@@ -36,6 +37,12 @@ CASES = [
     ("g8_bk16_b40_L1-70_halves_wide", 16, 2, 16, 40, ("uniform", 1, 70), 3, 16, 1024),
     ("g4_bk16_b100_L1-70_halves_wide", 16, 4, 16, 100, ("uniform", 1, 70), 7, 17, 1024),
     ("g8_bk16_b8192_L1-40_wide", 8, 1, 16, 8192, ("uniform", 1, 40), 100, 15, 1024),
+    # 128K-token contexts: one item of 4,096 sub-tiles cut between ~340 waves
+    # and merged in rounds of eight; two and six sequences whose items are
+    # cut into tens of pieces each
+    ("g8_bk16_b1_L131072", 8, 1, 16, 1, ("fixed", 131072), 0, 18),
+    ("g8_bk32_b2_L100k-128k", 64, 8, 32, 2, ("uniform", 100000, 131072), 0, 19),
+    ("g8_bk32_b6_L16-128k_log", 64, 8, 32, 6, ("loguniform", 16, 131072), 1, 35),
 ]
 
 
