@@ -81,3 +81,23 @@ def test_all_inactive_batch(gpu):
         o = outs[i].float().cpu().numpy()
         assert np.array_equal(o, np.zeros_like(o)) and not np.signbit(o).any(), f"layer {i}"
         assert np.array_equal(ref[i], np.zeros_like(ref[i]))
+
+
+def test_many_piece_merge_is_repeatable(gpu):
+    """One 131,072-token item cut between ~340 waves: five steps on the same
+    cache (each rewrites the same new token) give bitwise the same outputs
+    and the same cache, as every piece is cut at a fixed point and the pieces
+    merge in a fixed order whichever wave arrives last."""
+    import torch
+    cfg = Config("g8_bk16_b1_L131072_repeat", PAIR, 1, 8, 1, 64, 16, ("fixed", 131072), seed=18,
+                 max_ctx=131072)
+    wl = W.make_workload(cfg)
+    bufs = [h.to(gpu) for h in W.make_buffers(wl, "cpu")]
+    first, _ = gpu_step(wl, bufs, gpu)
+    after = [b.clone() for b in bufs]
+    for r in range(4):
+        outs, _ = gpu_step(wl, bufs, gpu)
+        for i in range(cfg.layers):
+            assert torch.equal(outs[i].view(torch.int16), first[i].view(torch.int16)), (r, i)
+        for j, b in enumerate(bufs):
+            assert torch.equal(b, after[j]), (r, j)
