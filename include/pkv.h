@@ -204,7 +204,9 @@ int64_t pkv_decode_workspace_bytes(int32_t batch, int32_t q_heads, int32_t kv_he
  * [nb, Hkv, block, head_dim] like V ("KV-cache layout"); same bytes, same speed.
  * rope_cos, rope_sin: fp32 [batch, head_dim/2] (16-byte aligned) or both NULL;
  * given, every query head of sequence b is first turned half-split by row b
- * (as in pkv_kv_cache_update), in fp32 and rounded to bf16 for the scores.
+ * (as in pkv_kv_cache_update), in fp32; the turned query enters the scores
+ * as two bf16 parts (its bf16 rounding and the remainder of that rounding),
+ * about 16 significant bits.
  * The cached keys are used as stored (a writer turned them before caching).
  * workspace: at least pkv_decode_workspace_bytes(...) bytes, 256-byte aligned,
  * zero-filled before first use. */
