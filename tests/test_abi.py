@@ -145,3 +145,23 @@ def test_noalloc_refuses_shapes_beyond_its_workspace():
     st = L.pkv_decode_layer_noalloc(ctypes.byref(s), 1, 0x1000, 0x1000, 0x1000, 0.125, 0.0625,
                                     0.125, 0x1000, None)
     assert st == P.PKV_ERR_WORKSPACE and b"library's own" in L.pkv_last_error()
+
+
+def test_error_text_is_per_thread():
+    """A call rejected on one thread sets that thread's error text only."""
+    import threading
+    lib = P.lib()
+    seen = {}
+
+    def bad():
+        seen["bad"] = (lib.pkv_trimmed_width(0, 16, 0), lib.pkv_last_error())  # window < 1
+
+    def good():
+        seen["good"] = (lib.pkv_trimmed_width(128, 16, 0), lib.pkv_last_error())
+
+    for f in (bad, good):
+        t = threading.Thread(target=f)
+        t.start()
+        t.join()
+    assert seen["bad"][0] < 0 and b"window" in seen["bad"][1]
+    assert seen["good"][0] == 9 and b"window" not in (seen["good"][1] or b"")
