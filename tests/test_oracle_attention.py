@@ -83,6 +83,22 @@ def test_window_equals_dense_over_last_128(Bk):
             assert np.allclose(out[b, g], ref, rtol=0, atol=1e-13)
 
 
+@pytest.mark.parametrize("Bk,W,lens", [(16, 1, [5, 1, 40]), (16, 33, [100, 33, 34]),
+                                        (32, 256, [600, 257, 300]), (64, 1000, [1300, 1001, 1100])])
+def test_window_equals_dense_over_the_last_w_keys(Bk, W, lens):
+    """Windows other than 128: the oracle attends exactly the last W keys."""
+    rng = np.random.default_rng(5)
+    B, Hq, H, D = 3, 4, 1, 64
+    c = _case(rng, B, Hq, H, Bk, D, lens)
+    ctl = C.attention_control(np.array(lens), np.ones(B, np.uint8), c["table"], c["table"], Bk, W)
+    out = A.paged_decode_attention(c["q"], c["kh"], c["vh"], ctl["bt_swa_trim"], ctl["pos_swa"],
+                                   W, Bk, H, 0.125, 0.0625, 0.125)
+    for b in range(B):
+        for g in range(Hq):
+            ref = _dense(c, b, g, Hq, max(0, lens[b] - W), lens[b] - 1, 0.125, 0.0625, 0.125)
+            assert np.allclose(out[b, g], ref, rtol=0, atol=1e-13)
+
+
 def test_window_equals_full_when_context_fits():
     rng = np.random.default_rng(3)
     B, Hq, H, Bk, D, W = 4, 8, 2, 16, 64, 128

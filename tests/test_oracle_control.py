@@ -11,19 +11,23 @@ GOLD = os.path.join(os.path.dirname(__file__), "golden")
 W = 128
 
 
-def _run(block, n_tok=3000):
+def _run(block, n_tok=3000, window=W):
     p = np.arange(n_tok)
     B = p.size
     width = -(-n_tok // block) + 1
     bt_full = np.tile(np.arange(width, dtype=np.int32) + 10_000, (B, 1))
     bt_swa = np.tile(np.arange(width, dtype=np.int32) + 50_000, (B, 1))
-    ctl = C.attention_control(p + 1, np.ones(B, np.uint8), bt_full, bt_swa, block, W)
+    ctl = C.attention_control(p + 1, np.ones(B, np.uint8), bt_full, bt_swa, block, window)
     return p, bt_full, bt_swa, ctl
 
 
-@pytest.mark.parametrize("block", [16, 32, 128])
-def test_trimmed_frame_covers_exactly_the_window(block):
-    p, bt_full, bt_swa, ctl = _run(block)
+# the pages' window of 128 at every supported block, and other windows (the
+# setup takes the window as an argument): 1 key, 33 keys, 1000 keys
+@pytest.mark.parametrize("block,window", [(16, 128), (32, 128), (128, 128), (16, 1), (16, 33),
+                                          (64, 33), (32, 1000), (64, 1000)])
+def test_trimmed_frame_covers_exactly_the_window(block, window):
+    W = window
+    p, bt_full, bt_swa, ctl = _run(block, 3000 if W < 1000 else 2500, W)
     n_swa = C.trimmed_width(W, block)
     assert ctl["bt_swa_trim"].shape[1] == n_swa
     for b in range(p.size):
