@@ -22,7 +22,14 @@ ATOL, RTOL = 2e-3, 1e-2
 #    The output is rounded to bf16 once (half an ulp); before that the only
 #    error above fp32 rounding is the fp16 rounding of the softmax weights
 #    fed to the PV product (relative 2^-11 per weight), which matters only
-#    where the output nearly cancels -- hence the absolute floor;
+#    where the output nearly cancels -- hence the absolute floor.  That error
+#    is at most 2^-11 times the weighted mean of |V| over the attended keys
+#    (sum_t w_t |v_t| / sum_t w_t), plus 2^-25 per weight that falls into the
+#    fp16 subnormals.  The fixed floor is a tripwire sized for the diffuse
+#    weights of N(0,1) queries over N(0,1) values, where that mean is about
+#    0.6-0.8 (at most 2.0 for a few elements of the 256-sequence workload) and
+#    almost no weight underflows; peaked weights need the derived per-element
+#    floor 2^-11 * (mean + 1), with the exact mean from `value_magnitude`;
 #  * aggregate: ||gpu - ref||_2 / ||ref||_2 <= L2_GUARD over all finite
 #    elements of a comparison.  bf16 rounding alone gives about 1.7e-3; a
 #    0.5% systematic error gives above 5e-3.
@@ -192,7 +199,28 @@ def bf16_ulp(x):
     return np.ldexp(1.0, e - 8)
 
 
-def assert_close(got_bf16, ref, what="", ulp_guard=ULP_GUARD, l2_guard=L2_GUARD):
+def value_magnitude(wl, snaps, k_packed=True):
+    """Per layer, sum_t w_t |v_t| / sum_t w_t for every output element: the
+    oracle's step over the same cache and new tokens with every V code's sign
+    bit cleared (E4M3 is sign-magnitude; 0x7F / 0xFF both stay NaN), which
+    leaves the weights unchanged.  snaps: pre-step host buffers (not
+    modified)."""
+    import dataclasses
+    half = wl.half_bytes
+    mags = []
+    for s in snaps:
+        m = s.copy()
+        m[half:] &= 0x7F
+        mags.append(m)
+    wl_abs = dataclasses.replace(wl, v_new=wl.v_new.abs())
+    out, _ = oracle_step(wl_abs, mags, k_packed=k_packed)
+    return out
+
+
+def assert_close(got_bf16, ref, what="", ulp_guard=ULP_GUARD, l2_guard=L2_GUARD,
+                 floor=FLOOR_GUARD):
+    """floor: the absolute part of the element-wise guard, a scalar or an
+    array shaped like ref (e.g. 2^-11 * value_magnitude(...))."""
     g = got_bf16.float().cpu().numpy().astype(np.float64)
     assert g.shape == ref.shape, (g.shape, ref.shape)
     err = np.abs(g - ref)
@@ -206,17 +234,17 @@ def assert_close(got_bf16, ref, what="", ulp_guard=ULP_GUARD, l2_guard=L2_GUARD)
     if not g.size:
         return 0.0
     ulp = bf16_ulp(ref)
-    ulps = np.max(np.maximum(err - FLOOR_GUARD, 0.0) / ulp)
+    ulps = np.max(np.maximum(err - floor, 0.0) / ulp)
     raw_ulps = np.max(err / ulp)
     l2 = float(np.sqrt(np.sum(err ** 2) / max(np.sum(ref ** 2), 1e-300)))
     STATS.append((what, float(err.max()), float(ulps), l2, float(raw_ulps)))
     print(f"[close] {what}: max abs {err.max():.2e}, max ulps beyond floor {ulps:.2f}, "
           f"max ulps {raw_ulps:.2f}, rel L2 {l2:.2e}", flush=True)
-    tight = err <= ulp_guard * ulp + FLOOR_GUARD if ulp_guard is not None else np.ones_like(err, bool)
+    tight = err <= ulp_guard * ulp + floor if ulp_guard is not None else np.ones_like(err, bool)
     if not tight.all():
         i = tuple(np.argwhere(~tight)[0])
         raise AssertionError(f"{what}: {int((~tight).sum())} of {tight.size} beyond "
-                             f"{ulp_guard} bf16 ulps + {FLOOR_GUARD:.1e}; first {list(i)} got {g[i]} "
+                             f"{ulp_guard} bf16 ulps + floor; first {list(i)} got {g[i]} "
                              f"ref {ref[i]}")
     assert l2 <= l2_guard, f"{what}: relative L2 error {l2:.3e} above {l2_guard:.1e}"
     return float(err.max())
